@@ -1,0 +1,193 @@
+"""Benchmark of the tree-verify MLA-absorb attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kimi] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one synthetic batch already resident in HBM:
+ancestor bitmasks from the parent array, the ragged plan, the attention kernel and the
+split combine.  The default workload is the Kimi/DeepSeekV3-shape request (H = 64 heads,
+latent 512 + rope 64, bf16, committed cache 4096 tokens, a 64-node best-first draft tree).
+
+One JSON line is printed.  `value` is algorithmic TFLOP/s of the whole step;
+`roofline` rates the attention kernel alone (HIP events on the stream it runs on) against
+the bf16 MFMA peak; `cpu_baseline` times the fp64 oracle on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
+PEAK_HBM_GBPS = 8000.0
+
+
+def tree_depth_sum(parents: np.ndarray) -> np.ndarray:
+    """Sum over nodes of the root-to-node path length (= visible tree keys), per request."""
+    B, N = parents.shape
+    depth = np.zeros((B, N), np.int64)
+    for b in range(B):
+        for i in range(N):
+            p = parents[b, i]
+            depth[b, i] = 1 + (depth[b, p] if p >= 0 else 0)
+    return depth.sum(axis=1)
+
+
+def algorithmic_work(inp: workloads.Inputs):
+    """(flops, bytes, cache_bytes) that the method must do: cache pairs plus visible tree pairs."""
+    sp = inp.spec
+    D, dc = sp.d_latent + sp.d_rope, sp.d_latent
+    e = 2 if sp.dtype == "bf16" else 4
+    R = sp.nodes * sp.heads
+    lens = inp.cache_lens.numpy().astype(np.int64)
+    vis_tree = tree_depth_sum(inp.parents.numpy())
+    flops = float(np.sum(2 * R * lens * (D + dc)) + np.sum(2 * sp.heads * (D + dc) * vis_tree))
+    W = (sp.nodes + 63) // 64
+    cache_bytes = float(lens.sum() * D * e)
+    by = cache_bytes + sp.batch * R * D * e + sp.batch * sp.nodes * D * e + sp.batch * sp.nodes * W * 8 \
+        + sp.batch * R * dc * 4
+    return flops, by, cache_bytes
+
+
+def run(args):
+    import tree_verify_mla_02_amd as kdt
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = workloads.make_inputs(args.workload, seed=args.seed)
+    sp = inp.spec
+    flops, nbytes, cache_bytes = algorithmic_work(inp)
+
+    parents = inp.parents.to(dev)
+    lens = inp.cache_lens.to(dev)
+    q_lat, q_rope = inp.q_lat.to(dev), inp.q_rope.to(dev)
+    kv, tkv = inp.kv_cache.to(dev), inp.tree_kv.to(dev)
+    dc = sp.d_latent
+    ckv, krope, tckv, tkrope = kv[:, :dc], kv[:, dc:], tkv[:, :, :dc], tkv[:, :, dc:]
+    maxL, total = int(inp.cache_lens.max()), inp.total_len
+    desc = kdt.make_desc(q_lat, q_rope, ckv, krope, tckv, tkrope, maxL, total)
+    ws = kdt.alloc_workspace(desc, dev)
+    masks = torch.empty((sp.batch, sp.nodes, (sp.nodes + 63) // 64), dtype=torch.int64, device=dev)
+    out = torch.empty((sp.batch, sp.nodes, sp.heads, dc), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kdt.build_visibility(parents, out=masks, dev_status=status, stream=stream)
+        kdt.plan(lens, desc, ws, dev_status=status, stream=stream)
+        kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
+        kdt.combine(out, desc, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise SystemExit(f"device status {int(status.item())} on the benchmark inputs")
+
+    # ---- timed region: K whole steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- the attention kernel alone, each launch bracketed by events on its stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kdt.combine(out, desc, ws, stream=stream)
+    torch.cuda.synchronize()
+
+    peak = PEAK_BF16_TFLOPS if sp.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    value = flops / (step_ms * 1e-3) / 1e12
+    line = {
+        "metric": "tree-verify attn TFLOP/s + cache GB/s, % of MI355X roofline, Kimi-shape N=64 tree",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sp.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, best-first draft tree)",
+        "config": {
+            "workload": f"{sp.name}: B={sp.batch} requests, N={sp.nodes} tree nodes, H={sp.heads} heads, "
+                        f"d_latent={sp.d_latent}, d_rope={sp.d_rope}, cache={maxL} tokens, {sp.dtype}",
+            "batch": sp.batch, "nodes": sp.nodes, "heads": sp.heads, "cache_len": maxL,
+            "total_cache_tokens": total, "tree": sp.tree, "splits": kdt.num_splits(desc),
+        },
+        "cache_gbps": round(cache_bytes / (step_ms * 1e-3) / 1e9, 2),
+        "alg_gflop_per_step": round(flops / 1e9, 4),
+        "alg_mbytes_per_step": round(nbytes / 1e6, 4),
+        "attn_kernel_ms": round(attn_ms, 5),
+        "wall_ms_timed_region": round(wall_ms, 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+        },
+    }
+    return line, inp
+
+
+def cpu_baseline(inp):
+    """The fp64 oracle on the host cores: masks + every output row of one step."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    flops, _, _ = algorithmic_work(inp)
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.run(inp, threads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"one whole step of the same workload (masks + all {inp.spec.batch * inp.spec.nodes * inp.spec.heads}"
+                      f" rows, fp64), {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="kimi", choices=sorted(workloads.SPECS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path runs on a single MI355X with no sharding "
+              "(see DESIGN.md for how it would shard); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    line, inp = run(args)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

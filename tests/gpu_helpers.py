@@ -1,0 +1,93 @@
+"""Shared helpers of the GPU tests: move a workloads.Inputs batch to the device and run the
+C-ABI path on it; pick sampled rows for oracle checks at full size."""
+from __future__ import annotations
+
+import dataclasses
+import sys
+
+import numpy as np
+import torch
+
+import tree_verify_mla_02_amd as kdt
+import workloads
+
+TOL = {"bf16": 2e-3, "f32": 1e-5}     # max-abs bounds on the fp32 outputs
+
+
+@dataclasses.dataclass
+class DevInputs:
+    parents: torch.Tensor
+    cache_lens: torch.Tensor
+    q_lat: torch.Tensor
+    q_rope: torch.Tensor
+    kv: torch.Tensor
+    tree_kv: torch.Tensor
+    dc: int
+
+    @property
+    def ckv(self):
+        return self.kv[:, : self.dc]
+
+    @property
+    def krope(self):
+        return self.kv[:, self.dc:]
+
+    @property
+    def tree_ckv(self):
+        return self.tree_kv[:, :, : self.dc]
+
+    @property
+    def tree_krope(self):
+        return self.tree_kv[:, :, self.dc:]
+
+
+def to_device(inp: workloads.Inputs) -> DevInputs:
+    kv = inp.kv_cache
+    if kv.shape[0] == 0:                        # keep a valid (aligned) allocation
+        kv = torch.zeros((1, kv.shape[1]), dtype=kv.dtype)
+    return DevInputs(parents=inp.parents.cuda(), cache_lens=inp.cache_lens.cuda(), q_lat=inp.q_lat.cuda(),
+                     q_rope=inp.q_rope.cuda(), kv=kv.cuda(), tree_kv=inp.tree_kv.cuda(), dc=inp.spec.d_latent)
+
+
+def run_gpu(inp: workloads.Inputs, dev: DevInputs = None, staged: bool = False):
+    """Masks [B,N,W] (numpy uint64) and outputs [B,N,H,d_c] (torch fp32, on device)."""
+    dev = dev or to_device(inp)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    masks = kdt.build_visibility(dev.parents, dev_status=status)
+    maxL = int(inp.cache_lens.max()) if inp.cache_lens.numel() else 0
+    total = inp.total_len
+    if not staged:
+        out = kdt.tree_verify_attn(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, masks,
+                                   dev.cache_lens, inp.scale, dev_status=status, max_cache_len=maxL,
+                                   total_cache_len=total)
+    else:
+        desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, maxL, total)
+        ws = kdt.alloc_workspace(desc)
+        out = torch.empty(dev.q_lat.shape, dtype=torch.float32, device="cuda")
+        kdt.plan(dev.cache_lens, desc, ws, dev_status=status)
+        kdt.attend(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, masks, inp.scale, out,
+                   desc, ws)
+        kdt.combine(out, desc, ws)
+    torch.cuda.synchronize()
+    return masks.cpu().numpy().view(np.uint64), out, int(status.item())
+
+
+def sample_rows(inp: workloads.Inputs, per_request: int = 12, seed: int = 0):
+    """Flat row ids: first/last row of every request, rows around 128-row tile edges, random rows."""
+    sp = inp.spec
+    R = sp.nodes * sp.heads
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(sp.batch):
+        base = b * R
+        cand = [0, R - 1, min(127, R - 1), min(128, R - 1), R // 2]
+        cand += list(rng.integers(0, R, size=per_request))
+        rows.update(base + int(c) for c in cand)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def report(name: str, err: float, tol: float):
+    line = f"{'PASS' if err <= tol else 'FAIL'} {name}: max-abs {err:.3e} (tol {tol:.0e})"
+    print(line, flush=True)
+    sys.stdout.flush()
+    return line

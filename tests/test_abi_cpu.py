@@ -1,0 +1,70 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every
+function include/kdt.h declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tree_verify_mla_02_amd as kdt
+from tree_verify_mla_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kdt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdt_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for need in ("kdt_build_visibility", "kdt_tree_verify_attn", "kdt_tree_verify_workspace_size"):
+        assert need in names
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kdt.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.kdt_version() == 1
+
+
+def test_status_strings():
+    lib = kdt.load()
+    assert lib.kdt_status_string(0) == b"KDT_OK"
+    assert lib.kdt_status_string(2) == b"KDT_ERR_UNSUPPORTED"
+    assert lib.kdt_status_string(99) == b"KDT_ERR_UNKNOWN"
+
+
+def test_visibility_rejects_bad_arguments_on_host():
+    lib = kdt.load()
+    assert lib.kdt_build_visibility(None, 1, 4, None, None, None) == _lib.KDT_ERR_INVALID_ARG
+    assert b"NULL" in lib.kdt_last_error()
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: the call fails before any launch
+    assert lib.kdt_build_visibility(fake, 1, 257, fake, None, None) == _lib.KDT_ERR_UNSUPPORTED
+    assert lib.kdt_build_visibility(fake, 1, 0, fake, None, None) == _lib.KDT_ERR_UNSUPPORTED
+    assert lib.kdt_build_visibility(fake, 0, 4, fake, None, None) == _lib.KDT_ERR_INVALID_ARG
+    assert lib.kdt_build_visibility(ctypes.c_void_p((1 << 20) + 2), 1, 4, fake, None, None) == _lib.KDT_ERR_MISALIGNED
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_nodes", 0, _lib.KDT_ERR_UNSUPPORTED), ("num_nodes", 300, _lib.KDT_ERR_UNSUPPORTED),
+    ("batch", 0, _lib.KDT_ERR_INVALID_ARG), ("num_heads", 0, _lib.KDT_ERR_INVALID_ARG),
+    ("d_latent", 256, _lib.KDT_ERR_UNSUPPORTED), ("dtype", 7, _lib.KDT_ERR_UNSUPPORTED),
+    ("ckv_stride", 500, _lib.KDT_ERR_INVALID_ARG), ("ckv_stride", 570, _lib.KDT_ERR_MISALIGNED), ("q_lat_stride", 516, _lib.KDT_ERR_MISALIGNED),
+    ("max_cache_len", -1, _lib.KDT_ERR_INVALID_ARG),
+])
+def test_desc_validation_on_host(field, value, code):
+    d = _lib.VerifyDesc(batch=1, num_nodes=8, num_heads=4, d_latent=512, d_rope=64, dtype=_lib.KDT_BF16,
+                        max_cache_len=16, total_cache_len=16, q_lat_stride=512, q_rope_stride=64, ckv_stride=576,
+                        krope_stride=576, tree_ckv_stride=576, tree_krope_stride=576)
+    setattr(d, field, value)
+    lib = kdt.load()
+    assert lib.kdt_tree_verify_num_splits(ctypes.byref(d)) == -1
+    assert lib.kdt_tree_verify_workspace_size(ctypes.byref(d)) == 0
+    assert lib.kdt_last_status() == code
+    assert lib.kdt_tree_verify_attn(*([None] * 8), ctypes.c_float(1.0), None, ctypes.byref(d), None, 0, None,
+                                    None) == code

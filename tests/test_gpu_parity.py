@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Masks must match bit for bit.  Outputs must match within max-abs 2e-3 for bf16 inputs
+(fp32 accumulate) and 1e-5 for fp32 inputs.  Every case prints a PASS/FAIL line with its
+error.  Full-size workloads compare every row where the oracle takes seconds, sampled rows
+(request edges, 128-row tile edges, random rows) elsewhere.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_verify_mla_02_amd as kdt
+import workloads
+from gpu_helpers import TOL, report, run_gpu, sample_rows, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def check(name, inp, rows=None, staged=False, dev=None):
+    print(f"case {name}: B={inp.spec.batch} N={inp.spec.nodes} H={inp.spec.heads} "
+          f"d=({inp.spec.d_latent},{inp.spec.d_rope}) {inp.spec.dtype} T={inp.total_len}", flush=True)
+    masks, out, status = run_gpu(inp, dev=dev, staged=staged)
+    ref_masks, bad = oracle.visibility(inp.parents.numpy())
+    np.testing.assert_array_equal(masks, ref_masks)
+    assert status == (kdt._lib.KDT_DEV_BAD_PARENT if bad else 0)
+    dc = inp.spec.d_latent
+    got = out.reshape(-1, dc).cpu().double().numpy()
+    ref = oracle.run(inp, rows=rows)[1].reshape(-1, dc)
+    if rows is not None:
+        got = got[rows]
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - ref).max()) if got.size else 0.0
+    tol = TOL[inp.spec.dtype]
+    report(name, err, tol)
+    assert err <= tol
+    return out
+
+
+# ------------------------------------------------------------------ the workload configs
+@pytest.mark.parametrize("name", ["tiny", "kimi", "block8", "decode"])
+def test_config_all_rows(name):
+    check(name, workloads.make_inputs(name, seed=0))
+
+
+@pytest.mark.parametrize("name", ["chain", "ragged", "wide"])
+def test_config_sampled_rows(name):
+    inp = workloads.make_inputs(name, seed=0)
+    check(name, inp, rows=sample_rows(inp, per_request=24 if name == "chain" else 8))
+
+
+def test_kimi_second_seed_staged():
+    inp = workloads.make_inputs("kimi", seed=1)
+    check("kimi-seed1-staged", inp, staged=True)
+
+
+# ------------------------------------------------------------------ small multi-tile cases (all rows)
+SMALL = {
+    # ragged tails everywhere: an empty cache, partial key tiles, a partial row tile
+    "ragged3": (workloads.Spec("ragged3", 40, 3, 20, 8, 512, 64, "bf16", None, ragged=(0, 300), tree="random"),
+                [0, 100, 257]),
+    # two mask words; H=3 so 32-row wave slices straddle nodes
+    "nodes65": (workloads.Spec("nodes65", 41, 2, 65, 3, 512, 64, "bf16", None, ragged=(1, 2000), tree="random"),
+                [64, 1000]),
+    # 256 nodes = four mask words, best-first tree
+    "nodes256": (workloads.Spec("nodes256", 42, 1, 256, 2, 512, 64, "bf16", 300, depth=16, topk=16), None),
+    # one request, few rows, long cache: split over many workgroups + combine, partial last split
+    "split": (workloads.Spec("split", 43, 1, 8, 16, 512, 64, "bf16", 3000, tree="random"), None),
+    "split_outliers": (workloads.Spec("split_o", 44, 2, 16, 8, 512, 64, "bf16", None, ragged=(500, 2500),
+                                      outlier_p=0.01, depth=16, topk=16), None),
+    "bf16_small_dims": (workloads.Spec("bsd", 45, 2, 9, 5, 64, 16, "bf16", None, ragged=(3, 80), tree="random"),
+                        [77, 3]),
+    "f32_ragged": (workloads.Spec("f32r", 46, 3, 30, 4, 64, 16, "f32", None, ragged=(0, 200), tree="random"),
+                   [0, 65, 200]),
+    "f32_split": (workloads.Spec("f32s", 47, 1, 8, 4, 64, 16, "f32", 5000, tree="random"), None),
+    "star": (workloads.Spec("star", 48, 2, 12, 8, 512, 64, "bf16", 130, tree="star"), None),
+    "chain_short": (workloads.Spec("chs", 49, 1, 16, 64, 512, 64, "bf16", 1000, tree="chain"), None),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_all_rows(name):
+    spec, lens = SMALL[name]
+    inp = workloads.make_inputs(spec, seed=0, cache_lens=None if lens is None else np.array(lens, np.int32))
+    check(name, inp)
+
+
+def test_chain_equals_causal_prefill_on_gpu():
+    """A chain tree over a cache is causal prefill over cache ++ chain (torch SDPA, fp64)."""
+    spec = workloads.Spec("chsdpa", 50, 1, 16, 4, 512, 64, "bf16", 700, tree="chain")
+    inp = workloads.make_inputs(spec, seed=0)
+    _, out, _ = run_gpu(inp)
+    L, N = 700, 16
+    k = torch.cat([inp.kv_cache, inp.tree_kv[0]]).double()
+    q = torch.cat([inp.q_lat[0], inp.q_rope[0]], -1).double().permute(1, 0, 2)   # [H, N, D]
+    causal = torch.arange(L + N)[None, :] <= (L + torch.arange(N))[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q[None], k[None, None].expand(1, 4, -1, -1), k[None, None, :, :512].expand(1, 4, -1, -1),
+        attn_mask=causal, scale=inp.scale)[0].permute(1, 0, 2)
+    err = float((out[0].cpu().double() - ref).abs().max())
+    report("chain==causal-prefill", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ edge cases and properties
+def test_invalid_parents_flag_and_zero_rows():
+    spec = workloads.Spec("badpar", 51, 2, 8, 4, 512, 64, "bf16", 100, tree="random")
+    par = workloads.make_parents(spec, 0)
+    par[0, 3] = 5          # parent after child
+    par[1, 6] = -7         # below -1
+    inp = workloads.make_inputs(spec, seed=0, parents=par)
+    masks, _, status = run_gpu(inp)
+    assert status & kdt._lib.KDT_DEV_BAD_PARENT
+    check("invalid-parents", inp)      # oracle zeroes the same rows
+
+
+def test_invalid_cache_lens_leave_out_untouched():
+    spec = workloads.Spec("badlen", 52, 2, 8, 4, 512, 64, "bf16", 100, tree="random")
+    inp = workloads.make_inputs(spec, seed=0)
+    dev = to_device(inp)
+    masks = kdt.build_visibility(dev.parents)
+    for lens, maxL in (([100, 101], 100), ([-1, 100], 100), ([100, 100], 100)):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        out = torch.full(dev.q_lat.shape, 7.0, dtype=torch.float32, device="cuda")
+        total = 150 if lens == [100, 100] else 200        # the last case overflows the packed rows
+        kdt.tree_verify_attn(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, masks,
+                             torch.tensor(lens, dtype=torch.int32, device="cuda"), inp.scale, out=out,
+                             dev_status=status, max_cache_len=maxL, total_cache_len=total)
+        torch.cuda.synchronize()
+        assert int(status.item()) & kdt._lib.KDT_DEV_CACHE_LEN, lens
+        assert bool((out == 7.0).all()), lens
+    print("PASS invalid-cache-lens: flagged, out untouched", flush=True)
+
+
+def test_invisible_nodes_do_not_matter():
+    """Perturbing the tree rows of siblings / descendants / cousins of node i leaves out[i] bit-identical."""
+    spec = workloads.Spec("invis", 53, 1, 40, 8, 512, 64, "bf16", 300, depth=6, topk=4)
+    inp = workloads.make_inputs(spec, seed=0)
+    masks, base, _ = run_gpu(inp)
+    par = inp.parents.numpy()[0]
+    rng = np.random.default_rng(0)
+    for i in rng.choice(40, size=6, replace=False):
+        anc, j = set(), int(i)
+        while j != -1:
+            anc.add(j)
+            j = int(par[j])
+        others = [j for j in range(40) if j not in anc]
+        pert = dataclasses.replace(inp, tree_kv=inp.tree_kv.clone())
+        pert.tree_kv[0, others] = (torch.randn(len(others), 576) * 3).to(torch.bfloat16)
+        _, out2, _ = run_gpu(pert)
+        assert torch.equal(out2[0, i], base[0, i]), i
+    print("PASS invisibility: outputs bit-identical under perturbation of invisible nodes", flush=True)
+
+
+def test_deterministic_and_permutation_exact():
+    inp = workloads.make_inputs(dataclasses.replace(workloads.SPECS["ragged"], batch=6), seed=2)
+    _, a, _ = run_gpu(inp)
+    _, b, _ = run_gpu(inp)
+    assert torch.equal(a, b)
+    perm = [3, 0, 5, 1, 4, 2]
+    _, c, _ = run_gpu(workloads.subset_requests(inp, perm))
+    assert torch.equal(c, a[perm])
+    print("PASS determinism + request permutation: bit-identical", flush=True)
+
+
+def test_request_alone_matches_batch():
+    inp = workloads.make_inputs(dataclasses.replace(workloads.SPECS["ragged"], batch=4), seed=3)
+    _, full, _ = run_gpu(inp)
+    for b in range(4):
+        _, solo, _ = run_gpu(workloads.subset_requests(inp, [b]))
+        err = float((solo[0] - full[b]).abs().max())
+        assert err <= TOL["bf16"], (b, err)
+    print("PASS request independence", flush=True)
+
+
+def test_abi_errors_on_device():
+    inp = workloads.make_inputs("tiny", seed=0)
+    dev = to_device(inp)
+    masks = kdt.build_visibility(dev.parents)
+    desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, 32)
+    ws = kdt.alloc_workspace(desc)
+    out = torch.empty(dev.q_lat.shape, dtype=torch.float32, device="cuda")
+    with pytest.raises(kdt.KdtError) as e:                      # workspace too small
+        kdt.plan(dev.cache_lens, desc, ws[:16], None)
+    assert e.value.code == kdt._lib.KDT_ERR_WORKSPACE
+    with pytest.raises(kdt.KdtError) as e:                      # misaligned pointer
+        kdt.attend(dev.q_lat.view(-1)[1:].view(-1)[: dev.q_lat.numel() - 1], dev.q_rope, dev.ckv, dev.krope,
+                   dev.tree_ckv, dev.tree_krope, masks, inp.scale, out, desc, ws)
+    assert e.value.code == kdt._lib.KDT_ERR_MISALIGNED
+    bad = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, 32)
+    bad.d_latent = 128
+    with pytest.raises(kdt.KdtError) as e:
+        kdt.workspace_size(bad)
+    assert e.value.code == kdt._lib.KDT_ERR_UNSUPPORTED
+    with pytest.raises(kdt.KdtError) as e:
+        kdt.build_visibility(torch.zeros((1, 257), dtype=torch.int32, device="cuda"))
+    assert e.value.code == kdt._lib.KDT_ERR_UNSUPPORTED
+    print("PASS ABI error paths", flush=True)

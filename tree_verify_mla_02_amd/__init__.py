@@ -1,0 +1,11 @@
+"""Tree-verify MLA-absorb attention for AMD MI355X (gfx950).
+
+The work runs in libkdt.so (hand-written HIP kernels behind the C ABI of include/kdt.h);
+this package is its Python binding.  Build the library with
+``python -m tree_verify_mla_02_amd.build``.
+"""
+from ._lib import (KdtError, VerifyDesc, alloc_workspace, attend, build_visibility, combine, load,
+                   make_desc, num_splits, plan, tree_verify_attn, workspace_size)
+
+__all__ = ["KdtError", "VerifyDesc", "alloc_workspace", "attend", "build_visibility", "combine", "load",
+           "make_desc", "num_splits", "plan", "tree_verify_attn", "workspace_size"]

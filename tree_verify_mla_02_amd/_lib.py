@@ -1,0 +1,209 @@
+"""ctypes binding of libkdt (include/kdt.h).  Argument marshalling only.
+
+Every computation runs in the HIP kernels of libkdt.so; torch only provides device memory
+and the current stream.  When the library is missing the calls raise -- there is no CPU
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkdt.so")
+
+KDT_OK, KDT_ERR_INVALID_ARG, KDT_ERR_UNSUPPORTED, KDT_ERR_MISALIGNED, KDT_ERR_WORKSPACE, KDT_ERR_HIP = range(6)
+KDT_DEV_BAD_PARENT, KDT_DEV_CACHE_LEN = 1, 2
+KDT_BF16, KDT_F32 = 0, 1
+
+EXPORTS = [
+    "kdt_build_visibility", "kdt_tree_verify_workspace_size", "kdt_tree_verify_attn",
+    "kdt_tree_verify_plan", "kdt_tree_verify_attend", "kdt_tree_verify_combine",
+    "kdt_tree_verify_num_splits", "kdt_status_string", "kdt_last_error", "kdt_last_status", "kdt_version",
+]
+
+
+class VerifyDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_nodes", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("max_cache_len", ctypes.c_int64), ("total_cache_len", ctypes.c_int64),
+        ("q_lat_stride", ctypes.c_int64), ("q_rope_stride", ctypes.c_int64),
+        ("ckv_stride", ctypes.c_int64), ("krope_stride", ctypes.c_int64),
+        ("tree_ckv_stride", ctypes.c_int64), ("tree_krope_stride", ctypes.c_int64),
+    ]
+
+
+class KdtError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_status_name(code)}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libkdt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m tree_verify_mla_02_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    dp = ctypes.POINTER(VerifyDesc)
+    lib.kdt_build_visibility.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.kdt_tree_verify_workspace_size.argtypes = [dp]
+    lib.kdt_tree_verify_workspace_size.restype = sz
+    lib.kdt_tree_verify_num_splits.argtypes = [dp]
+    lib.kdt_tree_verify_attn.argtypes = [vp] * 8 + [ctypes.c_float, vp, dp, vp, sz, vp, vp]
+    lib.kdt_tree_verify_plan.argtypes = [vp, dp, vp, sz, vp, vp]
+    lib.kdt_tree_verify_attend.argtypes = [vp] * 7 + [ctypes.c_float, vp, dp, vp, sz, vp]
+    lib.kdt_tree_verify_combine.argtypes = [vp, dp, vp, sz, vp]
+    lib.kdt_status_string.restype = ctypes.c_char_p
+    lib.kdt_last_error.restype = ctypes.c_char_p
+    for name in EXPORTS:
+        if name not in ("kdt_tree_verify_workspace_size", "kdt_status_string", "kdt_last_error"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _status_name(code: int) -> str:
+    try:
+        return load().kdt_status_string(code).decode()
+    except Exception:
+        return f"status {code}"
+
+
+def _check(code: int):
+    if code != KDT_OK:
+        raise KdtError(code, load().kdt_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    """Elements between consecutive rows of a tensor whose last dim is contiguous."""
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    lead = t.shape[:-1]
+    if len(lead) == 0 or t.numel() == 0:
+        return t.shape[-1]
+    # rows must be evenly spaced: every leading dim collapses into one row index
+    stride = t.stride(-2) if t.dim() >= 2 else t.shape[-1]
+    expect = stride
+    for d in range(t.dim() - 2, -1, -1):
+        if t.shape[d] > 1 and t.stride(d) != expect:
+            raise ValueError(f"{name}: rows are not evenly spaced (strides {t.stride()})")
+        expect *= t.shape[d]
+    return stride
+
+
+def make_desc(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, max_cache_len: int,
+              total_cache_len: Optional[int] = None) -> VerifyDesc:
+    B, N, H, dc = q_lat.shape
+    dr = q_rope.shape[-1]
+    if q_lat.dtype == torch.bfloat16:
+        dtype = KDT_BF16
+    elif q_lat.dtype == torch.float32:
+        dtype = KDT_F32
+    else:
+        raise ValueError(f"unsupported dtype {q_lat.dtype}")
+    for t, n in ((q_rope, "q_rope"), (ckv, "ckv"), (krope, "krope"), (tree_ckv, "tree_ckv"), (tree_krope, "tree_krope")):
+        if t.dtype != q_lat.dtype:
+            raise ValueError(f"{n} has dtype {t.dtype}, expected {q_lat.dtype}")
+    d = VerifyDesc()
+    d.batch, d.num_nodes, d.num_heads, d.d_latent, d.d_rope, d.dtype = B, N, H, dc, dr, dtype
+    d.max_cache_len = int(max_cache_len)
+    d.total_cache_len = int(ckv.shape[0] if total_cache_len is None else total_cache_len)
+    d.q_lat_stride = _row_stride(q_lat, "q_lat")
+    d.q_rope_stride = _row_stride(q_rope, "q_rope")
+    d.ckv_stride = _row_stride(ckv, "ckv")
+    d.krope_stride = _row_stride(krope, "krope")
+    d.tree_ckv_stride = _row_stride(tree_ckv, "tree_ckv")
+    d.tree_krope_stride = _row_stride(tree_krope, "tree_krope")
+    return d
+
+
+def workspace_size(desc: VerifyDesc) -> int:
+    n = load().kdt_tree_verify_workspace_size(ctypes.byref(desc))
+    if n == 0:
+        raise KdtError(load().kdt_last_status(), load().kdt_last_error().decode())
+    return n
+
+
+def num_splits(desc: VerifyDesc) -> int:
+    n = load().kdt_tree_verify_num_splits(ctypes.byref(desc))
+    if n < 0:
+        raise KdtError(load().kdt_last_status(), load().kdt_last_error().decode())
+    return n
+
+
+def alloc_workspace(desc: VerifyDesc, device=None) -> torch.Tensor:
+    # torch's caching allocator hands out 512-byte aligned blocks
+    return torch.empty(workspace_size(desc), dtype=torch.uint8, device=device or "cuda")
+
+
+def build_visibility(parents: torch.Tensor, out: Optional[torch.Tensor] = None,
+                     dev_status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """parents [B, N] int32 (device) -> ancestor bitmasks [B, N, ceil(N/64)] (int64 view of uint64)."""
+    if parents.dtype != torch.int32 or not parents.is_contiguous() or parents.dim() != 2:
+        raise ValueError("parents must be a contiguous [B, N] int32 tensor")
+    B, N = parents.shape
+    W = (N + 63) // 64
+    if out is None:
+        out = torch.empty((B, N, W), dtype=torch.int64, device=parents.device)
+    _check(load().kdt_build_visibility(_ptr(parents), B, N, _ptr(out), _ptr(dev_status), _stream(stream)))
+    return out
+
+
+def tree_verify_attn(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, bitmask, cache_lens, scale: float,
+                     out=None, workspace=None, dev_status=None, max_cache_len: Optional[int] = None,
+                     total_cache_len: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Tree-verify MLA-absorb attention; returns out [B, N, H, d_c] fp32.
+
+    max_cache_len is a host-side bound on cache_lens; when omitted it is read back from the
+    device (one synchronisation)."""
+    if max_cache_len is None:
+        max_cache_len = int(cache_lens.max().item()) if cache_lens.numel() else 0
+    desc = make_desc(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, max_cache_len, total_cache_len)
+    B, N, H, dc = q_lat.shape
+    if out is None:
+        out = torch.empty((B, N, H, dc), dtype=torch.float32, device=q_lat.device)
+    if workspace is None:
+        workspace = alloc_workspace(desc, q_lat.device)
+    _check(load().kdt_tree_verify_attn(
+        _ptr(q_lat), _ptr(q_rope), _ptr(ckv), _ptr(krope), _ptr(tree_ckv), _ptr(tree_krope), _ptr(bitmask),
+        _ptr(cache_lens), ctypes.c_float(scale), _ptr(out), ctypes.byref(desc), _ptr(workspace),
+        workspace.numel(), _ptr(dev_status), _stream(stream)))
+    return out
+
+
+def plan(cache_lens, desc: VerifyDesc, workspace, dev_status=None, stream=None):
+    _check(load().kdt_tree_verify_plan(_ptr(cache_lens), ctypes.byref(desc), _ptr(workspace), workspace.numel(),
+                                       _ptr(dev_status), _stream(stream)))
+
+
+def attend(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, bitmask, scale, out, desc: VerifyDesc, workspace,
+           stream=None):
+    _check(load().kdt_tree_verify_attend(_ptr(q_lat), _ptr(q_rope), _ptr(ckv), _ptr(krope), _ptr(tree_ckv),
+                                         _ptr(tree_krope), _ptr(bitmask), ctypes.c_float(scale), _ptr(out),
+                                         ctypes.byref(desc), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def combine(out, desc: VerifyDesc, workspace, stream=None):
+    _check(load().kdt_tree_verify_combine(_ptr(out), ctypes.byref(desc), _ptr(workspace), workspace.numel(),
+                                          _stream(stream)))

@@ -1,0 +1,324 @@
+// C ABI of libkdt: argument validation, launch geometry and dispatch.
+//
+// Every entry point checks what the host can see (pointers, sizes, alignment, workspace),
+// then enqueues kernels on the caller's stream and returns without synchronising.  No
+// exception crosses the ABI; errors are a kdt_status plus a thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kdt_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local int g_status = KDT_OK;
+
+int fail(int code, const char *fmt, ...) {
+    g_status = code;
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    g_status = KDT_OK;
+    return KDT_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(KDT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Compute units of the current device, cached per device id.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int current_cus(int *out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(KDT_ERR_HIP, "device id %d out of range", dev);
+    int n = g_cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+        if (n <= 0) n = 1;
+        g_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    *out = n;
+    return KDT_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int elem_size(int dtype) { return dtype == KDT_BF16 ? 2 : 4; }
+
+int check_desc(const kdt_verify_desc *d) {
+    if (!d) return fail(KDT_ERR_INVALID_ARG, "desc is NULL");
+    if (d->batch < 1) return fail(KDT_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", d->batch);
+    if (d->num_nodes < 1 || d->num_nodes > kdt::kMaxNodes)
+        return fail(KDT_ERR_UNSUPPORTED, "num_nodes must be in [1, %d] (got %d)", kdt::kMaxNodes, d->num_nodes);
+    if (d->num_heads < 1) return fail(KDT_ERR_INVALID_ARG, "num_heads must be >= 1 (got %d)", d->num_heads);
+    if (d->dtype != KDT_BF16 && d->dtype != KDT_F32) return fail(KDT_ERR_UNSUPPORTED, "unknown dtype %d", d->dtype);
+    const bool kimi = d->d_latent == 512 && d->d_rope == 64 && d->dtype == KDT_BF16;
+    const bool tiny = d->d_latent == 64 && d->d_rope == 16;
+    if (!kimi && !tiny)
+        return fail(KDT_ERR_UNSUPPORTED,
+                    "(d_latent, d_rope, dtype) = (%d, %d, %s) is not built; built: (512, 64, bf16), (64, 16, bf16), "
+                    "(64, 16, f32)",
+                    d->d_latent, d->d_rope, d->dtype == KDT_BF16 ? "bf16" : "f32");
+    if (d->max_cache_len < 0 || d->total_cache_len < 0)
+        return fail(KDT_ERR_INVALID_ARG, "cache length bounds must be >= 0");
+    if (d->max_cache_len > (int64_t)INT32_MAX) return fail(KDT_ERR_INVALID_ARG, "max_cache_len exceeds int32");
+    const int64_t epc = 16 / elem_size(d->dtype);
+    const struct { int64_t stride; int width; const char *name; } s[] = {
+        {d->q_lat_stride, d->d_latent, "q_lat_stride"},   {d->q_rope_stride, d->d_rope, "q_rope_stride"},
+        {d->ckv_stride, d->d_latent, "ckv_stride"},       {d->krope_stride, d->d_rope, "krope_stride"},
+        {d->tree_ckv_stride, d->d_latent, "tree_ckv_stride"}, {d->tree_krope_stride, d->d_rope, "tree_krope_stride"},
+    };
+    for (const auto &x : s) {
+        if (x.stride < x.width) return fail(KDT_ERR_INVALID_ARG, "%s = %lld is below the row width %d", x.name,
+                                            (long long)x.stride, x.width);
+        if (x.stride % epc) return fail(KDT_ERR_MISALIGNED, "%s = %lld is not a multiple of %lld elements (16 bytes)",
+                                        x.name, (long long)x.stride, (long long)epc);
+    }
+    return KDT_OK;
+}
+
+int geometry_for(const kdt_verify_desc *d, kdt::Geometry *g) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    int cus = 0;
+    rc = current_cus(&cus);
+    if (rc) return rc;
+    if (!kdt::make_geometry(*d, cus, g)) return fail(KDT_ERR_INVALID_ARG, "batch too large for one launch");
+    return KDT_OK;
+}
+
+int check_ws(const kdt::Geometry &g, const void *ws, size_t bytes) {
+    if (!ws) return fail(KDT_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)ws & 255u) return fail(KDT_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    if (bytes < g.total_bytes)
+        return fail(KDT_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", bytes, g.total_bytes);
+    return KDT_OK;
+}
+
+kdt::AttnArgs make_args(const kdt_verify_desc &d, const kdt::Geometry &g, void *ws) {
+    char *w = (char *)ws;
+    kdt::AttnArgs a{};
+    a.q_lat_stride = d.q_lat_stride;
+    a.q_rope_stride = d.q_rope_stride;
+    a.ckv_stride = d.ckv_stride;
+    a.krope_stride = d.krope_stride;
+    a.tckv_stride = d.tree_ckv_stride;
+    a.tkrope_stride = d.tree_krope_stride;
+    a.B = d.batch;
+    a.N = d.num_nodes;
+    a.H = d.num_heads;
+    a.W = g.mask_words;
+    a.R = g.rows;
+    a.RT = g.row_tiles;
+    a.S = g.nsplit;
+    a.chunk = g.chunk;
+    a.hdr = (const kdt::WsHeader *)(w + g.off_header);
+    a.offsets = (const int64_t *)(w + g.off_offsets);
+    a.lens = (const int32_t *)(w + g.off_lens);
+    a.units = (const int4 *)(w + g.off_units);
+    a.part_ml = g.off_ml ? (float2 *)(w + g.off_ml) : nullptr;
+    a.part_o = g.off_o ? (float *)(w + g.off_o) : nullptr;
+    return a;
+}
+
+}  // namespace
+
+namespace kdt {
+
+bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
+    Geometry x{};
+    x.rows = (int64_t)d.num_nodes * d.num_heads;
+    const int64_t rt = (x.rows + kRowsPerTile - 1) / kRowsPerTile;
+    if (rt > (1 << 30)) return false;
+    x.row_tiles = (int)rt;
+    x.mask_words = (d.num_nodes + 63) / 64;
+    const int64_t units0 = (int64_t)d.batch * rt;
+    const int64_t maxL = d.max_cache_len;
+    // Split the committed keys only when the batch alone cannot fill the GPU (about two
+    // workgroups per CU); keep every split at least kMinChunk keys so partials stay small
+    // next to the key traffic.
+    int64_t S = 1;
+    if (units0 < 2 * (int64_t)num_cus && maxL > kMinChunk) {
+        const int64_t want = ((int64_t)num_cus + units0 - 1) / units0;
+        const int64_t cap = (maxL + kMinChunk - 1) / kMinChunk;
+        S = want < cap ? want : cap;
+        if (S < 1) S = 1;
+    }
+    int64_t chunk = maxL > 0 ? (maxL + S - 1) / S : kKeysPerTile;
+    chunk = (chunk + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
+    if (chunk < kKeysPerTile) chunk = kKeysPerTile;
+    S = maxL > 0 ? (maxL + chunk - 1) / chunk : 1;
+    if (S < 1) S = 1;
+    x.nsplit = (int)S;
+    x.chunk = chunk;
+    x.units = units0 * S;
+    if (x.units > INT32_MAX) return false;
+    const int64_t B = d.batch;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = round_up(off + bytes, 256);
+        return o;
+    };
+    x.off_header = take(sizeof(WsHeader));
+    x.off_offsets = take(8 * B);
+    x.off_lens = take(4 * B);
+    x.off_order = take(4 * B);
+    x.off_base = take(8 * (B + 1));
+    x.off_units = take(16 * (size_t)x.units);
+    if (S > 1) {
+        x.off_ml = take(8 * (size_t)B * S * x.rows);
+        x.off_o = take(4 * (size_t)B * S * x.rows * d.d_latent);
+    } else {
+        x.off_ml = x.off_o = 0;
+    }
+    x.total_bytes = off;
+    *g = x;
+    return true;
+}
+
+}  // namespace kdt
+
+extern "C" {
+
+int kdt_version(void) { return KDT_VERSION; }
+
+const char *kdt_last_error(void) { return g_err; }
+
+int kdt_last_status(void) { return g_status; }
+
+const char *kdt_status_string(int status) {
+    switch (status) {
+        case KDT_OK: return "KDT_OK";
+        case KDT_ERR_INVALID_ARG: return "KDT_ERR_INVALID_ARG";
+        case KDT_ERR_UNSUPPORTED: return "KDT_ERR_UNSUPPORTED";
+        case KDT_ERR_MISALIGNED: return "KDT_ERR_MISALIGNED";
+        case KDT_ERR_WORKSPACE: return "KDT_ERR_WORKSPACE";
+        case KDT_ERR_HIP: return "KDT_ERR_HIP";
+        default: return "KDT_ERR_UNKNOWN";
+    }
+}
+
+int kdt_build_visibility(const int32_t *parents, int32_t batch, int32_t num_nodes, uint64_t *bitmask,
+                         int32_t *dev_status, void *stream) {
+    if (!parents || !bitmask) return fail(KDT_ERR_INVALID_ARG, "parents and bitmask must not be NULL");
+    if (batch < 1) return fail(KDT_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (num_nodes < 1 || num_nodes > kdt::kMaxNodes)
+        return fail(KDT_ERR_UNSUPPORTED, "num_nodes must be in [1, %d] (got %d)", kdt::kMaxNodes, num_nodes);
+    if (((uintptr_t)parents & 3u) || ((uintptr_t)bitmask & 7u))
+        return fail(KDT_ERR_MISALIGNED, "parents must be 4-byte and bitmask 8-byte aligned");
+    if ((int64_t)batch * num_nodes > (int64_t)INT32_MAX * 128) return fail(KDT_ERR_INVALID_ARG, "batch too large");
+    const hipError_t e = kdt::launch_visibility(parents, batch, num_nodes, bitmask, dev_status, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "visibility launch");
+    return ok();
+}
+
+size_t kdt_tree_verify_workspace_size(const kdt_verify_desc *desc) {
+    kdt::Geometry g;
+    if (geometry_for(desc, &g)) return 0;
+    ok();
+    return g.total_bytes;
+}
+
+int kdt_tree_verify_num_splits(const kdt_verify_desc *desc) {
+    kdt::Geometry g;
+    if (geometry_for(desc, &g)) return -1;
+    ok();
+    return g.nsplit;
+}
+
+int kdt_tree_verify_plan(const int32_t *cache_lens, const kdt_verify_desc *desc, void *workspace,
+                         size_t workspace_bytes, int32_t *dev_status, void *stream) {
+    kdt::Geometry g;
+    int rc = geometry_for(desc, &g);
+    if (rc) return rc;
+    if (!cache_lens) return fail(KDT_ERR_INVALID_ARG, "cache_lens is NULL");
+    if ((uintptr_t)cache_lens & 3u) return fail(KDT_ERR_MISALIGNED, "cache_lens must be 4-byte aligned");
+    rc = check_ws(g, workspace, workspace_bytes);
+    if (rc) return rc;
+    const hipError_t e = kdt::launch_plan(cache_lens, *desc, g, workspace, dev_status, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    return ok();
+}
+
+int kdt_tree_verify_attend(const void *q_lat, const void *q_rope, const void *ckv_cache, const void *krope_cache,
+                           const void *tree_ckv, const void *tree_krope, const uint64_t *bitmask, float scale,
+                           float *out, const kdt_verify_desc *desc, void *workspace, size_t workspace_bytes,
+                           void *stream) {
+    kdt::Geometry g;
+    int rc = geometry_for(desc, &g);
+    if (rc) return rc;
+    const void *ptrs[] = {q_lat, q_rope, ckv_cache, krope_cache, tree_ckv, tree_krope, bitmask, out};
+    const char *names[] = {"q_lat", "q_rope", "ckv_cache", "krope_cache", "tree_ckv", "tree_krope", "bitmask", "out"};
+    for (int k = 0; k < 8; k++) {
+        // the cache pointers may be NULL only when there is no committed row at all
+        if (!ptrs[k] && !((k == 2 || k == 3) && desc->total_cache_len == 0))
+            return fail(KDT_ERR_INVALID_ARG, "%s is NULL", names[k]);
+        if (!aligned16(ptrs[k])) return fail(KDT_ERR_MISALIGNED, "%s is not 16-byte aligned", names[k]);
+    }
+    if (!std::isfinite(scale)) return fail(KDT_ERR_INVALID_ARG, "scale must be finite");
+    rc = check_ws(g, workspace, workspace_bytes);
+    if (rc) return rc;
+    kdt::AttnArgs a = make_args(*desc, g, workspace);
+    a.q_lat = q_lat;
+    a.q_rope = q_rope;
+    a.ckv = ckv_cache;
+    a.krope = krope_cache;
+    a.tckv = tree_ckv;
+    a.tkrope = tree_krope;
+    a.masks = bitmask;
+    a.out = out;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const hipError_t e = kdt::launch_attend(a, desc->d_latent, desc->d_rope, desc->dtype, g.units, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ok();
+}
+
+int kdt_tree_verify_combine(float *out, const kdt_verify_desc *desc, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    kdt::Geometry g;
+    int rc = geometry_for(desc, &g);
+    if (rc) return rc;
+    if (!out) return fail(KDT_ERR_INVALID_ARG, "out is NULL");
+    if (!aligned16(out)) return fail(KDT_ERR_MISALIGNED, "out is not 16-byte aligned");
+    rc = check_ws(g, workspace, workspace_bytes);
+    if (rc) return rc;
+    if (g.nsplit <= 1) return ok();
+    kdt::AttnArgs a = make_args(*desc, g, workspace);
+    a.out = out;
+    const hipError_t e = kdt::launch_combine(a, desc->d_latent, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    return ok();
+}
+
+int kdt_tree_verify_attn(const void *q_lat, const void *q_rope, const void *ckv_cache, const void *krope_cache,
+                         const void *tree_ckv, const void *tree_krope, const uint64_t *bitmask,
+                         const int32_t *cache_lens, float scale, float *out, const kdt_verify_desc *desc,
+                         void *workspace, size_t workspace_bytes, int32_t *dev_status, void *stream) {
+    int rc = kdt_tree_verify_plan(cache_lens, desc, workspace, workspace_bytes, dev_status, stream);
+    if (rc) return rc;
+    rc = kdt_tree_verify_attend(q_lat, q_rope, ckv_cache, krope_cache, tree_ckv, tree_krope, bitmask, scale, out,
+                                desc, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return kdt_tree_verify_combine(out, desc, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal declarations of libkdt shared by the C-ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "../../include/kdt.h"
+
+namespace kdt {
+
+// Work decomposition of the verify attention.
+//   A work unit is (request b, row tile rt, key split s).  A row tile is 128 query rows
+//   (4 waves x 32 rows, rows node-major r = i*H + h); a key split is a contiguous range of
+//   `chunk` committed-cache keys.  Split 0 of every request also owns its tree segment.
+constexpr int kWaves = 4;
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerTile = kWaves * kRowsPerWave;   // 128
+constexpr int kKeysPerTile = 64;                       // one LDS tile = 64 keys
+constexpr int kMaxNodes = 256;                         // 4 mask words
+constexpr int kMinChunk = 256;                         // a split covers at least 4 tiles
+
+struct Geometry {
+    int64_t rows;          // R = N * H query rows per request
+    int row_tiles;         // RT = ceil(R / 128)
+    int nsplit;            // S: splits per request at most (1 = no split)
+    int64_t chunk;         // committed keys per split
+    int64_t units;         // grid size of the attention kernel = B * RT * S
+    int mask_words;        // W = ceil(N / 64)
+    // workspace layout (byte offsets, 256-aligned)
+    size_t off_header, off_offsets, off_lens, off_order, off_base, off_units, off_ml, off_o, total_bytes;
+};
+
+// Fills g from desc for a device with `num_cus` compute units.  Returns false on overflow.
+bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g);
+
+// Workspace header written by the plan kernel.
+struct WsHeader {
+    int32_t ok;            // 1 when cache_lens passed the device checks
+    int32_t pad[63];
+};
+
+struct AttnArgs {
+    const void *q_lat, *q_rope, *ckv, *krope, *tckv, *tkrope;
+    const uint64_t *masks;
+    float *out;
+    int64_t q_lat_stride, q_rope_stride, ckv_stride, krope_stride, tckv_stride, tkrope_stride;
+    int B, N, H, W;
+    int64_t R;
+    int RT, S;
+    int64_t chunk;
+    float scale_log2;      // scale * log2(e): scores are kept in the base-2 domain
+    const WsHeader *hdr;
+    const int64_t *offsets;
+    const int32_t *lens;
+    const int4 *units;     // (b, rt, s, splits of b); b < 0 marks an empty slot
+    float2 *part_ml;       // [B][S][R] (running max in log2 domain, sum)
+    float *part_o;         // [B][S][R][d_c] un-normalised partial outputs
+};
+
+hipError_t launch_visibility(const int32_t *parents, int B, int N, uint64_t *masks,
+                             int32_t *dev_status, hipStream_t st);
+hipError_t launch_plan(const int32_t *cache_lens, const kdt_verify_desc &d, const Geometry &g,
+                       void *ws, int32_t *dev_status, hipStream_t st);
+hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units,
+                         hipStream_t st);
+hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st);
+
+}  // namespace kdt

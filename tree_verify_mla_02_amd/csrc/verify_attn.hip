@@ -1,0 +1,518 @@
+// Tree-verify MLA-absorb attention for gfx950 (MI355X).
+//
+// What is computed ("Validating the Native Engine", section "The Broader Context": a
+// tree-verify MLA-absorb attention kernel with visibility masking; "The Capstone
+// Validation", section "Context and Motivation": all drafted continuations are verified in
+// one batched pass): for request b, tree node i and head h,
+//     out[b,i,h] = softmax_k(scale * (q_lat.ckv_k + q_rope.krope_k)) . ckv_k
+// over the request's committed cache and the tree nodes on i's root-to-node path.
+//
+// How it maps to CDNA4.  In absorbed MLA every head reads the same latent rows, so the
+// (node x head) query rows of a request form the M dimension of one dense contraction
+// against shared 576-wide key rows -- exactly the shape bf16 MFMA is built for.
+//   * A workgroup is 4 waves x 32 query rows (128 rows).  A wave keeps its queries in
+//     VGPRs (B operand of S^T = K Q^T) and its 32 x d_c fp32 output accumulator O^T in the
+//     MFMA result registers for the whole key loop.
+//   * Key rows stream HBM -> LDS in 64-key tiles with global_load_lds_dwordx4 (no VGPR
+//     staging), double buffered.  The LDS tile is stored in 1 KB blocks of (keys x 16-byte
+//     chunks) with an XOR swizzle of the chunk index by the key, so that both the row-wise
+//     K reads of S^T = K Q^T and the column-wise V reads of O^T = V^T P^T are free of bank
+//     conflicts.
+//   * Scores come out of the MFMA transposed (one query row per lane pair), so the online
+//     softmax needs one cross-lane exchange per tile; P^T feeds the P.V MFMA directly from
+//     the score registers, and V^T comes from LDS through ds_read_b64_tr_b16.
+//   * P is split into bf16 hi + lo parts, both multiplied by V (fp32 accumulate): this
+//     keeps the probability weights ~16 bits accurate, which a single bf16 rounding of P
+//     is not when a few keys with large latent values dominate a row.
+//   * The tree segment is one more tile (or up to four for 256 nodes) whose scores are
+//     masked with the row's 64-bit ancestor word.
+//   * Small batches split the committed keys over workgroups; partial (O, max, sum) are
+//     merged by a log-sum-exp combine.
+#include "kdt_internal.h"
+
+namespace kdt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// Splits used for request b: split 0 always exists (it owns the tree keys).
+__device__ __forceinline__ int splits_of(int L, int64_t chunk, int S) {
+    if (L <= 0) return 1;
+    const int64_t n = (L + chunk - 1) / chunk;
+    return (int)(n < S ? n : S);
+}
+
+// ------------------------------------------------------------------------------ plan
+// One workgroup.  Validates cache_lens, writes per-request offsets (exclusive scan), a
+// longest-first order of requests and the unit list the attention grid reads: request by
+// request, and inside a request split-fastest, so that the units sharing one key split are
+// 8 apart in the grid and land on the same XCD (the dispatcher deals workgroups to the 8
+// XCDs round-robin); their key tiles are then read from one L2.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ cache_lens, int B,
+                                                    int64_t max_len, int64_t total_len, int RT, int S,
+                                                    int64_t chunk, int64_t U, WsHeader *hdr,
+                                                    int64_t *offsets, int32_t *lens, int32_t *order,
+                                                    int64_t *base, int4 *units, int32_t *dev_status) {
+    __shared__ int s_ok;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_ok = 1;
+    __syncthreads();
+    for (int b = tid; b < B; b += blockDim.x) {
+        const int L = cache_lens[b];
+        lens[b] = L;
+        if (L < 0 || (int64_t)L > max_len) s_ok = 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int64_t off = 0;
+        for (int b = 0; b < B; b++) {
+            offsets[b] = off;
+            off += lens[b] > 0 ? lens[b] : 0;
+        }
+        if (off > total_len) s_ok = 0;
+    }
+    __syncthreads();
+    const int ok = s_ok;
+    // rank = number of requests that go first: longer ones, then equal ones with lower index
+    for (int b = tid; b < B; b += blockDim.x) {
+        const int L = lens[b];
+        int rank = 0;
+        for (int c = 0; c < B; c++) {
+            const int Lc = lens[c];
+            rank += (Lc > L) || (Lc == L && c < b);
+        }
+        order[rank] = b;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int64_t acc = 0;
+        for (int p = 0; p < B; p++) {
+            base[p] = acc;
+            acc += (int64_t)RT * (ok ? splits_of(lens[order[p]], chunk, S) : 0);
+        }
+        base[B] = acc;
+        hdr->ok = ok;
+        if (!ok && dev_status) atomicOr(dev_status, (int32_t)KDT_DEV_CACHE_LEN);
+    }
+    __syncthreads();
+    const int64_t used = base[B];
+    for (int64_t u = tid; u < U; u += blockDim.x) {
+        int4 d = make_int4(-1, 0, 0, 0);
+        if (u < used) {
+            int lo = 0, hi = B - 1;          // last p with base[p] <= u
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (base[mid] <= u) lo = mid; else hi = mid - 1;
+            }
+            const int b = order[lo];
+            const int sb = splits_of(lens[b], chunk, S);
+            const int64_t v = u - base[lo];
+            d = make_int4(b, (int)(v / sb), (int)(v % sb), sb);
+        }
+        units[u] = d;
+    }
+}
+
+// ------------------------------------------------------------------------------ attention
+template <typename T, int DC, int DR>
+struct Shape {
+    static constexpr int D = DC + DR;
+    static constexpr int ES = (int)sizeof(T);
+    static constexpr int EPC = 16 / ES;             // elements per 16-byte chunk
+    static constexpr int CH = D / EPC;              // chunks per key row
+    static constexpr int CH_LAT = DC / EPC;         // chunks of the latent part
+    static constexpr int CB = (CH % 8 == 0) ? 8 : (CH % 4 == 0) ? 4 : 2;   // chunks per LDS block row
+    static constexpr int KB = 64 / CB;              // keys per 1 KB LDS block
+    static constexpr int NKG = kKeysPerTile / KB;   // key groups per tile
+    static constexpr int NCG = CH / CB;             // chunk groups per key row
+    static constexpr int TILE_BYTES = kKeysPerTile * D * ES;
+    static constexpr bool BF16 = (ES == 2);
+    static_assert(D % EPC == 0 && CH % CB == 0 && CH_LAT % CB == 0, "row must split into blocks");
+    static_assert(TILE_BYTES == NKG * NCG * 1024, "tile = whole 1 KB blocks");
+    static_assert(DC % 32 == 0, "latent width must be a multiple of 32");
+    static_assert(!BF16 || (DC % 16 == 0 && DR % 16 == 0), "bf16 K steps are 16 wide");
+    static_assert(BF16 || (DC % 4 == 0 && DR % 4 == 0), "fp32 rows are whole chunks");
+};
+
+// Byte offset of logical 16-byte chunk c of tile key `key` inside one LDS tile buffer.
+template <class Sh>
+__device__ __forceinline__ int lds_off(int key, int c) {
+    const int kg = key / Sh::KB, kr = key % Sh::KB;
+    const int cg = c / Sh::CB, cc = c % Sh::CB;
+    return ((kg * Sh::NCG + cg) << 10) + kr * (Sh::CB * 16) + ((cc ^ (kr % Sh::CB)) << 4);
+}
+
+// Offset of tile key `k` (a multiple of 8) relative to key k % 8 with the same chunk: the
+// XOR swizzle only looks at key % CB (CB <= 8), so it is unchanged.
+template <class Sh>
+__host__ __device__ constexpr int key_off(int k) {
+    return (k / Sh::KB) * Sh::NCG * 1024 + (k % Sh::KB) * Sh::CB * 16;
+}
+
+// Issue this wave's share of one 64-key tile: rows row0 .. row0+63 of (lat | rope), keys at
+// or beyond nvalid re-read the last valid row (their scores are masked; the data only has
+// to be finite).  Lane l fills 16-byte slot l of a 1 KB block.
+template <class Sh, typename T>
+__device__ __forceinline__ void issue_tile(LDS_AS char *buf, const T *__restrict__ lat, int64_t lat_stride,
+                                           const T *__restrict__ rope, int64_t rope_stride, int64_t row0,
+                                           int nvalid, int wave, int lane) {
+    const int kr = lane / Sh::CB;
+    const int cc = (lane % Sh::CB) ^ (kr % Sh::CB);
+    for (int kg = wave; kg < Sh::NKG; kg += kWaves) {
+        int key = kg * Sh::KB + kr;
+        key = key < nvalid ? key : nvalid - 1;
+        const T *lrow = lat + (row0 + key) * lat_stride;
+        const T *rrow = rope + (row0 + key) * rope_stride;
+#pragma unroll
+        for (int cg = 0; cg < Sh::NCG; cg++) {
+            const int c = cg * Sh::CB + cc;
+            const T *src = (cg * Sh::CB < Sh::CH_LAT) ? lrow + c * Sh::EPC : rrow + (c - Sh::CH_LAT) * Sh::EPC;
+            __builtin_amdgcn_global_load_lds((const void *)src,
+                                             (LDS_AS void *)(buf + ((kg * Sh::NCG + cg) << 10)), 16, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// O^T *= alpha (one scale per lane = per query row), done in place in the accumulation
+// registers.  Written as AGPR read / VALU multiply / AGPR write so the 32 x d_c accumulator
+// never needs a VGPR home: a plain `o *= alpha` makes the register allocator move the whole
+// accumulator into VGPRs and spill.  The leading s_nops cover the wait states between an
+// MFMA writing an accumulator and a v_accvgpr_read of it, the trailing one those between
+// v_accvgpr_write and the next MFMA reading it as srcC.
+template <int NT>
+__device__ __forceinline__ void rescale_acc(f32x16 (&o)[NT], float alpha) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            float tmp;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(o[t][i]), "=&v"(tmp)
+                         : "v"(alpha));
+        }
+    asm volatile("s_nop 7" ::: "memory");
+}
+
+template <typename T, int DC, int DR>
+__global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
+    using Sh = Shape<T, DC, DR>;
+    constexpr int D = Sh::D;
+    constexpr int NT16 = DC / 32;                       // 32-wide output column tiles
+    constexpr int NQ = Sh::BF16 ? D / 16 : D / 2;       // query fragments per lane
+    __shared__ __attribute__((aligned(1024))) char smem[2 * Sh::TILE_BYTES];
+
+    if (!a.hdr->ok) return;
+    const int4 unit = a.units[blockIdx.x];
+    if (unit.x < 0) return;
+    const int b = unit.x, rt = unit.y, s = unit.z, sb = unit.w;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = lane >> 5;                          // 0: lanes 0-31, 1: lanes 32-63
+    const int64_t R = a.R;
+
+    // ---- this lane's query row (lanes l and l+32 share row l%32 of the wave)
+    const int64_t r = (int64_t)rt * kRowsPerTile + wave * kRowsPerWave + (lane & 31);
+    const bool row_ok = r < R;
+    const int64_t rc = row_ok ? r : R - 1;
+    const int node = (int)(rc / a.H);
+    const T *qlat = (const T *)a.q_lat + ((int64_t)b * R + rc) * a.q_lat_stride;
+    const T *qrope = (const T *)a.q_rope + ((int64_t)b * R + rc) * a.q_rope_stride;
+
+    // ---- key ranges: cache keys [k0, k1) of this split, then the tree keys if s == 0
+    const int L = a.lens[b];
+    const int64_t k0 = (int64_t)s * a.chunk;
+    const int64_t k1 = (k0 + a.chunk < (int64_t)L) ? k0 + a.chunk : (int64_t)L;
+    const int n_cache = k1 > k0 ? (int)(((k1 - k0) + kKeysPerTile - 1) / kKeysPerTile) : 0;
+    const int n_tree = (s == 0) ? (a.N + kKeysPerTile - 1) / kKeysPerTile : 0;
+    const int n_tiles = n_cache + n_tree;
+    const int64_t cache_row0 = a.offsets[b] + k0;
+
+    auto issue = [&](int t) {
+        LDS_AS char *buf = (LDS_AS char *)smem + (t & 1) * Sh::TILE_BYTES;
+        if (t < n_cache) {
+            const int64_t row0 = cache_row0 + (int64_t)t * kKeysPerTile;
+            const int64_t left = k1 - k0 - (int64_t)t * kKeysPerTile;
+            issue_tile<Sh, T>(buf, (const T *)a.ckv, a.ckv_stride, (const T *)a.krope, a.krope_stride, row0,
+                              left < kKeysPerTile ? (int)left : kKeysPerTile, wave, lane);
+        } else {
+            const int tt = t - n_cache;
+            const int left = a.N - tt * kKeysPerTile;
+            issue_tile<Sh, T>(buf, (const T *)a.tckv, a.tckv_stride, (const T *)a.tkrope, a.tkrope_stride,
+                              (int64_t)b * a.N + (int64_t)tt * kKeysPerTile,
+                              left < kKeysPerTile ? left : kKeysPerTile, wave, lane);
+        }
+    };
+    issue(0);
+
+    // ---- queries to registers: B operand of S^T = K Q^T
+    typedef typename std::conditional<Sh::BF16, bf16x8, float>::type QFrag;
+    QFrag q[NQ];
+    if constexpr (Sh::BF16) {
+#pragma unroll
+        for (int kk = 0; kk < NQ; kk++) {
+            const int d0 = 16 * kk + 8 * half;
+            const T *src = (16 * kk < DC) ? qlat + d0 : qrope + (d0 - DC);
+            q[kk] = *(const bf16x8 *)src;
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < NQ; kk++) {
+            const int d = 2 * kk + half;
+            q[kk] = (2 * kk < DC) ? (float)qlat[d] : (float)qrope[d - DC];
+        }
+    }
+
+    // per-lane LDS byte offsets (see lds_off) of the few swizzle patterns this lane reads
+    constexpr int QK_PAT = Sh::CB / 2;                       // K reads: chunk 2kk + half
+    constexpr int PV_PAT = Sh::CB >= 8 ? Sh::CB / 4 : 1;     // V^T reads: chunk 4*t16 + y
+    int qk_base[QK_PAT], pv_base[PV_PAT];
+#pragma unroll
+    for (int j = 0; j < QK_PAT; j++) qk_base[j] = lds_off<Sh>(lane & 31, 2 * j + half);
+    {
+        const int w = 4 * half + ((lane & 15) >> 2);              // key within an 8-key group
+        const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within 4 chunks (32 columns)
+#pragma unroll
+        for (int j = 0; j < PV_PAT; j++) pv_base[j] = lds_off<Sh>(w, 4 * j + y) + 8 * (lane & 1);
+    }
+
+    f32x16 o[NT16];
+#pragma unroll
+    for (int t = 0; t < NT16; t++) o[t] = (f32x16){};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int t = 0; t < n_tiles; t++) {
+        wait_vm_all();
+        __syncthreads();                 // tile t is in LDS; every wave is done with tile t-1
+        if (t + 1 < n_tiles) issue(t + 1);
+        const LDS_AS char *buf = (const LDS_AS char *)smem + (t & 1) * Sh::TILE_BYTES;
+
+        // ---- S^T = K Q^T : two 32-key blocks, rows of this wave as N
+        f32x16 sc[2];
+        sc[0] = (f32x16){};
+        sc[1] = (f32x16){};
+        if constexpr (Sh::BF16) {
+            // chunk 2kk+half of key kb*32 + lane%32: the swizzle pattern repeats every CB/2
+            // steps of kk, the rest is a compile-time offset folded into ds_read_b128.
+            const LDS_AS char *pq[QK_PAT];
+#pragma unroll
+            for (int j = 0; j < QK_PAT; j++) pq[j] = buf + qk_base[j];
+#pragma unroll
+            for (int kk = 0; kk < NQ; kk++) {
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++) {
+                    const bf16x8 ka = *(const LDS_AS bf16x8 *)(pq[kk % QK_PAT] + key_off<Sh>(kb * 32) +
+                                                               (kk / QK_PAT) * 1024);
+                    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q[kk], sc[kb], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < NQ; kk++) {
+                const int d = 2 * kk + half;
+#pragma unroll
+                for (int kb = 0; kb < 2; kb++) {
+                    const float ka =
+                        *(const LDS_AS float *)(buf + lds_off<Sh>(kb * 32 + (lane & 31), d >> 2) + ((d & 3) << 2));
+                    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, q[kk], sc[kb], 0, 0, 0);
+                }
+            }
+        }
+
+        // ---- mask: lane holds keys kb*32 + (i/4)*8 + 4*half + i%4 of its row
+        const bool is_tree = t >= n_cache;
+        int nvalid;
+        uint64_t word = ~0ull;
+        if (!is_tree) {
+            const int64_t left = k1 - k0 - (int64_t)t * kKeysPerTile;
+            nvalid = left < kKeysPerTile ? (int)left : kKeysPerTile;
+        } else {
+            const int tt = t - n_cache;
+            nvalid = a.N - tt * kKeysPerTile;
+            word = a.masks[((int64_t)b * a.N + node) * a.W + tt];
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const int key = kb * 32 + (i >> 2) * 8 + 4 * half + (i & 3);
+                const bool vis = key < nvalid && ((word >> key) & 1ull);
+                const float x = vis ? sc[kb][i] * a.scale_log2 : -INFINITY;
+                sc[kb][i] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+
+        // ---- online softmax (base 2)
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const float p = __builtin_amdgcn_exp2f(sc[kb][i] - m_use);
+                sc[kb][i] = p;
+                psum += p;
+            }
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        if (__ballot(alpha != 1.f)) rescale_acc<NT16>(o, alpha);
+
+        // ---- O^T += V^T P^T
+        if constexpr (Sh::BF16) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ks++) {         // 16 keys per step
+                const int kb = ks >> 1, h16 = ks & 1;
+                bf16x8 phi, plo;
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    const float p = sc[kb][8 * h16 + j];
+                    const __bf16 hi = (__bf16)p;
+                    phi[j] = hi;
+                    plo[j] = (__bf16)(p - (float)hi);
+                }
+                const int kbase = kb * 32 + 16 * h16;
+#pragma unroll
+                for (int t16 = 0; t16 < NT16; t16++) {
+                    // keys kbase + 4*half + (lane%16)/4 (+8), columns t16*32 + 16*((lane/16)%2) + 4*(lane%4)
+                    const LDS_AS char *pv = buf + pv_base[(4 * t16 % Sh::CB) / 4] + (4 * t16 / Sh::CB) * 1024;
+                    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (LDS_AS bf16x4 *)(pv + key_off<Sh>(kbase)));
+                    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (LDS_AS bf16x4 *)(pv + key_off<Sh>(kbase + 8)));
+                    const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, phi, o[t16], 0, 0, 0);
+                    o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, plo, o[t16], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; kb++) {
+#pragma unroll
+                for (int i = 0; i < 16; i++) {
+                    const int key = kb * 32 + (i >> 2) * 8 + 4 * half + (i & 3);
+#pragma unroll
+                    for (int t16 = 0; t16 < NT16; t16++) {
+                        const int dc = t16 * 32 + (lane & 31);
+                        const float va =
+                            *(const LDS_AS float *)(buf + lds_off<Sh>(key, dc >> 2) + ((dc & 3) << 2));
+                        o[t16] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, sc[kb][i], o[t16], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: lane holds O^T[dc = t16*32 + (i/4)*8 + 4*half + i%4][row]
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!row_ok) return;
+    if (sb == 1) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float *dst = a.out + ((int64_t)b * R + r) * DC;
+#pragma unroll
+        for (int t16 = 0; t16 < NT16; t16++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const float4 v = make_float4(o[t16][4 * g] * inv, o[t16][4 * g + 1] * inv, o[t16][4 * g + 2] * inv,
+                                             o[t16][4 * g + 3] * inv);
+                *(float4 *)(dst + t16 * 32 + g * 8 + 4 * half) = v;
+            }
+    } else {
+        const int64_t prow = ((int64_t)b * a.S + s) * R + r;
+        float *dst = a.part_o + prow * DC;
+#pragma unroll
+        for (int t16 = 0; t16 < NT16; t16++)
+#pragma unroll
+            for (int g = 0; g < 4; g++)
+                *(float4 *)(dst + t16 * 32 + g * 8 + 4 * half) =
+                    make_float4(o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2], o[t16][4 * g + 3]);
+        if (half == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
+    }
+}
+
+// ------------------------------------------------------------------------------ combine
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, for rows of split
+// requests.  One wave per row; lane handles 8 consecutive output columns.
+template <int DC>
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+    if (!a.hdr->ok) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)a.B * a.R) return;
+    const int b = (int)(row / a.R);
+    const int64_t r = row - (int64_t)b * a.R;
+    const int sb = splits_of(a.lens[b], a.chunk, a.S);
+    if (sb <= 1) return;
+    const int64_t prow0 = (int64_t)b * a.S * a.R + r;
+    float M = -INFINITY;
+    for (int s = 0; s < sb; s++) M = fmaxf(M, a.part_ml[prow0 + (int64_t)s * a.R].x);
+    constexpr int PER = 8;
+    if (lane * PER >= DC) return;
+    float acc[PER];
+#pragma unroll
+    for (int k = 0; k < PER; k++) acc[k] = 0.f;
+    float den = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < sb; s++) {
+            const int64_t prow = prow0 + (int64_t)s * a.R;
+            const float2 ml = a.part_ml[prow];
+            const float w = __builtin_amdgcn_exp2f(ml.x - M);
+            den += w * ml.y;
+            const float4 *src = (const float4 *)(a.part_o + prow * DC + lane * PER);
+            const float4 x0 = src[0], x1 = src[1];
+            acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
+            acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+        }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    float4 *dst = (float4 *)(a.out + row * DC + lane * PER);
+    dst[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+}
+
+// ------------------------------------------------------------------------------ launchers
+hipError_t launch_plan(const int32_t *cache_lens, const kdt_verify_desc &d, const Geometry &g, void *ws,
+                       int32_t *dev_status, hipStream_t st) {
+    char *w = (char *)ws;
+    plan_kernel<<<1, 1024, 0, st>>>(cache_lens, d.batch, d.max_cache_len, d.total_cache_len, g.row_tiles,
+                                    g.nsplit, g.chunk, g.units, (WsHeader *)(w + g.off_header),
+                                    (int64_t *)(w + g.off_offsets), (int32_t *)(w + g.off_lens),
+                                    (int32_t *)(w + g.off_order), (int64_t *)(w + g.off_base),
+                                    (int4 *)(w + g.off_units), dev_status);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units, hipStream_t st) {
+    const dim3 grid((unsigned)units), block(256);
+    if (dtype == KDT_BF16 && d_latent == 512 && d_rope == 64)
+        verify_attn_kernel<__bf16, 512, 64><<<grid, block, 0, st>>>(a);
+    else if (dtype == KDT_BF16 && d_latent == 64 && d_rope == 16)
+        verify_attn_kernel<__bf16, 64, 16><<<grid, block, 0, st>>>(a);
+    else if (dtype == KDT_F32 && d_latent == 64 && d_rope == 16)
+        verify_attn_kernel<float, 64, 16><<<grid, block, 0, st>>>(a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st) {
+    const int64_t rows = (int64_t)a.B * a.R;
+    const unsigned grid = (unsigned)((rows + 3) / 4);
+    if (d_latent == 512)
+        combine_kernel<512><<<grid, 256, 0, st>>>(a);
+    else if (d_latent == 64)
+        combine_kernel<64><<<grid, 256, 0, st>>>(a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace kdt
