@@ -198,6 +198,169 @@ __device__ __forceinline__ void rescale_acc(f32x16 (&o)[NT], float alpha) {
     asm volatile("s_nop 7" ::: "memory");
 }
 
+// ------------------------------------------------------------------------------ softmax
+// Online softmax of one query row over 32-key blocks, in base 2 (scores times scale*log2 e).
+// Probabilities are taken relative to a reference max m_ref that moves only when the row
+// max exceeds it by more than kLazy: O and l are then rescaled (rare).  Otherwise P stays
+// below 2^kLazy, which fp32 and the bf16 hi/lo pair represent with the same relative
+// accuracy as P <= 1, so the result is the same softmax without a rescale per tile.
+constexpr float kLazy = 8.f;
+
+struct Update {
+    float m_use;    // reference the block's probabilities are taken against (0 if none yet)
+    float alpha;    // factor for O and l accumulated so far (1 = unchanged)
+};
+
+// lane holds keys kb*32 + (i/4)*8 + 4*half + i%4 (i = 0..15) of its row
+__device__ __forceinline__ bool key_visible(int kb, int i, int half, int nvalid, uint64_t word) {
+    const int key = kb * 32 + (i >> 2) * 8 + 4 * half + (i & 3);
+    return key < nvalid && ((word >> key) & 1ull);
+}
+
+struct SoftmaxRow {
+    float m_ref;    // reference max (base-2 domain), -inf until the row sees a key
+    float l;        // running sum of probabilities relative to m_ref (this lane's keys only)
+    float c;        // scale * log2(e)
+
+    __device__ __forceinline__ Update update(const f32x16 &s, int kb, int half, bool need_mask, int nvalid,
+                                             uint64_t word) {
+        // extreme raw score in the direction of c (max for c >= 0), masked keys excluded
+        const bool neg = c < 0.f;
+        float e;
+        if (!neg) {
+            e = -INFINITY;
+            if (need_mask) {
+#pragma unroll
+                for (int i = 0; i < 16; i++) e = fmaxf(e, key_visible(kb, i, half, nvalid, word) ? s[i] : -INFINITY);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; i++) e = fmaxf(e, s[i]);
+            }
+        } else {
+            e = INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                e = fminf(e, (!need_mask || key_visible(kb, i, half, nvalid, word)) ? s[i] : INFINITY);
+        }
+        const float o2 = __shfl_xor(e, 32);                    // the other half of the row
+        e = neg ? fminf(e, o2) : fmaxf(e, o2);
+        const bool any = neg ? (e != INFINITY) : (e != -INFINITY);
+        const float mx = any ? e * c : -INFINITY;
+        const bool upd = mx > m_ref + kLazy;                   // also true for the first visible key
+        const float m_new = upd ? mx : m_ref;
+        const float alpha = (upd && m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+        m_ref = m_new;
+        return Update{m_new == -INFINITY ? 0.f : m_new, alpha};
+    }
+
+    // P = 2^(s*c - m) as bf16 hi + lo pairs (B operands of the two P.V MFMAs); returns sum P
+    __device__ __forceinline__ float probs(f32x16 &s, const Update &u, int kb, int half, bool need_mask, int nvalid,
+                                           uint64_t word, bf16x8 (&phi)[2], bf16x8 (&plo)[2]) const {
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -u.m_use));
+            if (need_mask) p = key_visible(kb, i, half, nvalid, word) ? p : 0.f;
+            sum += p;
+            const __bf16 hi = (__bf16)p;
+            phi[i >> 3][i & 7] = hi;
+            plo[i >> 3][i & 7] = (__bf16)(p - (float)hi);
+        }
+        return sum;
+    }
+
+    __device__ __forceinline__ float probs_f32(f32x16 &s, const Update &u, int kb, int half, bool need_mask,
+                                               int nvalid, uint64_t word) const {
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -u.m_use));
+            if (need_mask) p = key_visible(kb, i, half, nvalid, word) ? p : 0.f;
+            s[i] = p;
+            sum += p;
+        }
+        return sum;
+    }
+};
+
+// ------------------------------------------------------------------------------ MFMA blocks
+// The S^T chain keeps its accumulator in VGPRs (the softmax reads it with VALU ops) while the
+// 256 AGPRs hold O^T.  Compiler-selected MFMAs in a kernel that uses AGPRs all write AGPRs,
+// which would push part of O^T out, so these MFMAs are written out with explicit register
+// classes.  The wait states the compiler would insert are spelled out: 2 between dependent
+// 32x32x16 MFMAs on the same accumulator (s_nop 1), 12 or more before a VALU instruction
+// reads the result (s_nop 7 + s_nop 4 after the last one).  The first MFMA takes srcC = 0.
+__device__ __forceinline__ void mfma_s_first(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\ts_nop 1" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_next(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 1" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_s_last(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 4" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// S^T for 32 keys (block kb of the tile) x this wave's 32 rows: NQ MFMA 32x32x16, with the
+// K fragments read from LDS QD steps ahead of the MFMA that consumes them.
+template <class Sh, int NQ>
+__device__ __forceinline__ f32x16 qk_block(const LDS_AS char *buf, int kb, const bf16x8 (&q)[NQ],
+                                           const int (&qk_base)[Sh::CB / 2]) {
+    constexpr int PAT = Sh::CB / 2;
+    constexpr int QD = 6;
+    static_assert(NQ >= 2, "chain needs a first and a last MFMA");
+    const LDS_AS char *pq[PAT];
+#pragma unroll
+    for (int j = 0; j < PAT; j++) pq[j] = buf + qk_base[j] + key_off<Sh>(kb * 32);
+    auto load = [&](int kk) { return *(const LDS_AS bf16x8 *)(pq[kk % PAT] + (kk / PAT) * 1024); };
+    bf16x8 kf[QD];
+#pragma unroll
+    for (int j = 0; j < QD && j < NQ; j++) kf[j] = load(j);
+    f32x16 acc;
+#pragma unroll
+    for (int kk = 0; kk < NQ; kk++) {
+        if (kk == 0)
+            mfma_s_first(acc, kf[0], q[0]);
+        else if (kk == NQ - 1)
+            mfma_s_last(acc, kf[kk % QD], q[kk]);
+        else
+            mfma_s_next(acc, kf[kk % QD], q[kk]);
+        if (kk + QD < NQ) kf[kk % QD] = load(kk + QD);
+    }
+    return acc;
+}
+
+// O^T += V^T P^T for 32 keys (block kb): for each 16-key step and 32-column tile, one V^T
+// fragment (two ds_read_b64_tr_b16) feeds the hi and the lo MFMA.  Fragments are read kPD
+// steps ahead; column tiles go in pairs so consecutive MFMAs use different accumulators.
+template <class Sh, int NT16>
+__device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const bf16x8 (&phi)[2],
+                                         const bf16x8 (&plo)[2], f32x16 (&o)[NT16],
+                                         const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1]) {
+    constexpr int NSTEP = 2 * NT16;     // (h16, t16) pairs
+    constexpr int PD = 4;
+    auto load = [&](int st) {
+        const int h16 = st / NT16, t16 = st % NT16;
+        const int kbase = kb * 32 + 16 * h16;
+        const LDS_AS char *pv = buf + pv_base[(4 * t16 % Sh::CB) / 4] + (4 * t16 / Sh::CB) * 1024;
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(pv + key_off<Sh>(kbase)));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(pv + key_off<Sh>(kbase + 8)));
+        return (bf16x8)__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vf[PD];
+#pragma unroll
+    for (int j = 0; j < PD; j++) vf[j] = load(j);
+#pragma unroll
+    for (int st = 0; st < NSTEP; st += 2) {
+        const int h16 = st / NT16, t16 = st % NT16;
+        o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], phi[h16], o[t16], 0, 0, 0);
+        o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], phi[h16], o[t16 + 1], 0, 0, 0);
+        o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], plo[h16], o[t16], 0, 0, 0);
+        o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], plo[h16], o[t16 + 1], 0, 0, 0);
+        if (st + PD < NSTEP) vf[st % PD] = load(st + PD);
+        if (st + 1 + PD < NSTEP) vf[(st + 1) % PD] = load(st + 1 + PD);
+    }
+}
+
 template <typename T, int DC, int DR>
 __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     using Sh = Shape<T, DC, DR>;
@@ -282,7 +445,7 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     f32x16 o[NT16];
 #pragma unroll
     for (int t = 0; t < NT16; t++) o[t] = (f32x16){};
-    float m_run = -INFINITY, l_run = 0.f;
+    SoftmaxRow sm{-INFINITY, 0.f, a.scale_log2};
 
     for (int t = 0; t < n_tiles; t++) {
         wait_vm_all();
@@ -290,39 +453,7 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
         if (t + 1 < n_tiles) issue(t + 1);
         const LDS_AS char *buf = (const LDS_AS char *)smem + (t & 1) * Sh::TILE_BYTES;
 
-        // ---- S^T = K Q^T : two 32-key blocks, rows of this wave as N
-        f32x16 sc[2];
-        sc[0] = (f32x16){};
-        sc[1] = (f32x16){};
-        if constexpr (Sh::BF16) {
-            // chunk 2kk+half of key kb*32 + lane%32: the swizzle pattern repeats every CB/2
-            // steps of kk, the rest is a compile-time offset folded into ds_read_b128.
-            const LDS_AS char *pq[QK_PAT];
-#pragma unroll
-            for (int j = 0; j < QK_PAT; j++) pq[j] = buf + qk_base[j];
-#pragma unroll
-            for (int kk = 0; kk < NQ; kk++) {
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++) {
-                    const bf16x8 ka = *(const LDS_AS bf16x8 *)(pq[kk % QK_PAT] + key_off<Sh>(kb * 32) +
-                                                               (kk / QK_PAT) * 1024);
-                    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, q[kk], sc[kb], 0, 0, 0);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < NQ; kk++) {
-                const int d = 2 * kk + half;
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++) {
-                    const float ka =
-                        *(const LDS_AS float *)(buf + lds_off<Sh>(kb * 32 + (lane & 31), d >> 2) + ((d & 3) << 2));
-                    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, q[kk], sc[kb], 0, 0, 0);
-                }
-            }
-        }
-
-        // ---- mask: lane holds keys kb*32 + (i/4)*8 + 4*half + i%4 of its row
+        // ---- which keys of this tile the row sees: a full cache tile needs no mask
         const bool is_tree = t >= n_cache;
         int nvalid;
         uint64_t word = ~0ull;
@@ -334,68 +465,40 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             nvalid = a.N - tt * kKeysPerTile;
             word = a.masks[((int64_t)b * a.N + node) * a.W + tt];
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const int key = kb * 32 + (i >> 2) * 8 + 4 * half + (i & 3);
-                const bool vis = key < nvalid && ((word >> key) & 1ull);
-                const float x = vis ? sc[kb][i] * a.scale_log2 : -INFINITY;
-                sc[kb][i] = x;
-                mx = fmaxf(mx, x);
-            }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool need_mask = is_tree || nvalid < kKeysPerTile;
 
-        // ---- online softmax (base 2)
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float psum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++) {
-#pragma unroll
-            for (int i = 0; i < 16; i++) {
-                const float p = __builtin_amdgcn_exp2f(sc[kb][i] - m_use);
-                sc[kb][i] = p;
-                psum += p;
-            }
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (__ballot(alpha != 1.f)) rescale_acc<NT16>(o, alpha);
-
-        // ---- O^T += V^T P^T
         if constexpr (Sh::BF16) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ks++) {         // 16 keys per step
-                const int kb = ks >> 1, h16 = ks & 1;
-                bf16x8 phi, plo;
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    const float p = sc[kb][8 * h16 + j];
-                    const __bf16 hi = (__bf16)p;
-                    phi[j] = hi;
-                    plo[j] = (__bf16)(p - (float)hi);
-                }
-                const int kbase = kb * 32 + 16 * h16;
-#pragma unroll
-                for (int t16 = 0; t16 < NT16; t16++) {
-                    // keys kbase + 4*half + (lane%16)/4 (+8), columns t16*32 + 16*((lane/16)%2) + 4*(lane%4)
-                    const LDS_AS char *pv = buf + pv_base[(4 * t16 % Sh::CB) / 4] + (4 * t16 / Sh::CB) * 1024;
-                    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (LDS_AS bf16x4 *)(pv + key_off<Sh>(kbase)));
-                    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                        (LDS_AS bf16x4 *)(pv + key_off<Sh>(kbase + 8)));
-                    const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, phi, o[t16], 0, 0, 0);
-                    o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, plo, o[t16], 0, 0, 0);
-                }
-            }
+            // Two 32-key halves.  The softmax VALU work of one half sits in the same basic
+            // block as MFMAs of the other (QK of half 1, then P.V of half 0), so it can issue
+            // while the matrix core is busy.
+            f32x16 s0 = qk_block<Sh, NQ>(buf, 0, q, qk_base);
+            const Update u0 = sm.update(s0, 0, half, need_mask, nvalid, word);
+            f32x16 s1 = qk_block<Sh, NQ>(buf, 1, q, qk_base);
+            bf16x8 p0hi[2], p0lo[2];
+            const float l0 = sm.probs(s0, u0, 0, half, need_mask, nvalid, word, p0hi, p0lo);
+            if (__ballot(u0.alpha != 1.f)) rescale_acc<NT16>(o, u0.alpha);
+            pv_block<Sh, NT16>(buf, 0, p0hi, p0lo, o, pv_base);
+            const Update u1 = sm.update(s1, 1, half, need_mask, nvalid, word);
+            bf16x8 p1hi[2], p1lo[2];
+            const float l1 = sm.probs(s1, u1, 1, half, need_mask, nvalid, word, p1hi, p1lo);
+            sm.l = (sm.l * u0.alpha + l0) * u1.alpha + l1;
+            if (__ballot(u1.alpha != 1.f)) rescale_acc<NT16>(o, u1.alpha);
+            pv_block<Sh, NT16>(buf, 1, p1hi, p1lo, o, pv_base);
         } else {
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
+                f32x16 sc = (f32x16){};
+#pragma unroll
+                for (int kk = 0; kk < NQ; kk++) {
+                    const int d = 2 * kk + half;
+                    const float ka =
+                        *(const LDS_AS float *)(buf + lds_off<Sh>(kb * 32 + (lane & 31), d >> 2) + ((d & 3) << 2));
+                    sc = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, q[kk], sc, 0, 0, 0);
+                }
+                const Update u = sm.update(sc, kb, half, need_mask, nvalid, word);
+                const float lsum = sm.probs_f32(sc, u, kb, half, need_mask, nvalid, word);
+                sm.l = sm.l * u.alpha + lsum;
+                if (__ballot(u.alpha != 1.f)) rescale_acc<NT16>(o, u.alpha);
 #pragma unroll
                 for (int i = 0; i < 16; i++) {
                     const int key = kb * 32 + (i >> 2) * 8 + 4 * half + (i & 3);
@@ -404,12 +507,13 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
                         const int dc = t16 * 32 + (lane & 31);
                         const float va =
                             *(const LDS_AS float *)(buf + lds_off<Sh>(key, dc >> 2) + ((dc & 3) << 2));
-                        o[t16] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, sc[kb][i], o[t16], 0, 0, 0);
+                        o[t16] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, sc[i], o[t16], 0, 0, 0);
                     }
                 }
             }
         }
     }
+    const float m_run = sm.m_ref, l_run = sm.l;
 
     // ---- epilogue: lane holds O^T[dc = t16*32 + (i/4)*8 + 4*half + i%4][row]
     const float l_tot = l_run + __shfl_xor(l_run, 32);
