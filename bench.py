@@ -178,11 +178,22 @@ def main():
     ap.add_argument("--workload", default="kimi", choices=sorted(workloads.SPECS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X with no sharding "
               "(see DESIGN.md for how it would shard); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_direction": n, "launches": args.steps}), flush=True)
+        return
     line, inp = run(args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)

@@ -6,7 +6,7 @@
 
 #include <type_traits>
 
-#include "../../include/kdt.h"
+#include "kdt.h"
 
 namespace kdt {
 

@@ -37,6 +37,19 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define LDS_AS __attribute__((address_space(3)))
 
+template <int I>
+struct IntC {
+    static constexpr int value = I;
+};
+// Compile-time loop: f(IntC<B>), ..., f(IntC<E-1>).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(IntC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // Splits used for request b: split 0 always exists (it owns the tree keys).
 __device__ __forceinline__ int splits_of(int L, int64_t chunk, int S) {
     if (L <= 0) return 1;
@@ -129,6 +142,16 @@ struct Shape {
     static constexpr int NCG = CH / CB;             // chunk groups per key row
     static constexpr int TILE_BYTES = kKeysPerTile * D * ES;
     static constexpr bool BF16 = (ES == 2);
+    // XOR applied to the 16-byte chunk index of a key row inside its 1 KB block.  gfx950 LDS
+    // serves a 16-byte-per-lane read 16 lanes at a time over 64 four-byte banks (256 B).
+    // With 8-chunk rows (CB = 8) the 16 lanes of an S^T fragment read keys k..k+15 at one
+    // chunk: rows of even / odd key land in the two 128-byte bank halves, and bits 1..3 of
+    // the key pick distinct chunk slots within a half.  Bit 1 drives the top bit of the XOR,
+    // so the transposed V^T reads (keys r and r+2 of a 4-key group, 4 chunks each) also fall
+    // in opposite slot halves.  Both read patterns are conflict-free.  Only key % 16 matters.
+    static __host__ __device__ constexpr int swz(int key) {
+        return CB == 8 ? ((((key >> 1) & 1) << 2) | (((key >> 2) & 1) << 1) | ((key >> 3) & 1)) : (key % KB) % CB;
+    }
     static_assert(D % EPC == 0 && CH % CB == 0 && CH_LAT % CB == 0, "row must split into blocks");
     static_assert(TILE_BYTES == NKG * NCG * 1024, "tile = whole 1 KB blocks");
     static_assert(DC % 32 == 0, "latent width must be a multiple of 32");
@@ -141,11 +164,11 @@ template <class Sh>
 __device__ __forceinline__ int lds_off(int key, int c) {
     const int kg = key / Sh::KB, kr = key % Sh::KB;
     const int cg = c / Sh::CB, cc = c % Sh::CB;
-    return ((kg * Sh::NCG + cg) << 10) + kr * (Sh::CB * 16) + ((cc ^ (kr % Sh::CB)) << 4);
+    return ((kg * Sh::NCG + cg) << 10) + kr * (Sh::CB * 16) + ((cc ^ Sh::swz(key)) << 4);
 }
 
-// Offset of tile key `k` (a multiple of 8) relative to key k % 8 with the same chunk: the
-// XOR swizzle only looks at key % CB (CB <= 8), so it is unchanged.
+// Offset of tile key `k` (a multiple of 16) relative to key k % 16 with the same chunk: the
+// swizzle only looks at key % 16, so it is unchanged.
 template <class Sh>
 __host__ __device__ constexpr int key_off(int k) {
     return (k / Sh::KB) * Sh::NCG * 1024 + (k % Sh::KB) * Sh::CB * 16;
@@ -159,10 +182,10 @@ __device__ __forceinline__ void issue_tile(LDS_AS char *buf, const T *__restrict
                                            const T *__restrict__ rope, int64_t rope_stride, int64_t row0,
                                            int nvalid, int wave, int lane) {
     const int kr = lane / Sh::CB;
-    const int cc = (lane % Sh::CB) ^ (kr % Sh::CB);
     for (int kg = wave; kg < Sh::NKG; kg += kWaves) {
-        int key = kg * Sh::KB + kr;
-        key = key < nvalid ? key : nvalid - 1;
+        const int slot_key = kg * Sh::KB + kr;                    // the key this LDS slot holds
+        const int cc = (lane % Sh::CB) ^ Sh::swz(slot_key);      // its logical chunk
+        const int key = slot_key < nvalid ? slot_key : nvalid - 1;
         const T *lrow = lat + (row0 + key) * lat_stride;
         const T *rrow = rope + (row0 + key) * rope_stride;
 #pragma unroll
@@ -211,56 +234,63 @@ struct Update {
     float alpha;    // factor for O and l accumulated so far (1 = unchanged)
 };
 
-// lane holds keys kb*32 + (i/4)*8 + 4*half + i%4 (i = 0..15) of its row
-__device__ __forceinline__ bool key_visible(int kb, int i, int half, int nvalid, uint64_t word) {
-    const int key = kb * 32 + (i >> 2) * 8 + 4 * half + (i & 3);
-    return key < nvalid && ((word >> key) & 1ull);
+// Visibility of the 16 keys a lane holds in one 32-key block: bit (i/4)*8 + i%4 of
+// `w` is key kb*32 + (i/4)*8 + 4*half + i%4.  `vis` is the tile's 64-bit visibility word
+// (ancestor word of the row's node for tree tiles, all ones for cache tiles) with the keys at
+// or beyond the valid count already cleared.
+__device__ __forceinline__ uint32_t block_bits(uint64_t vis, int kb, int half) {
+    return (uint32_t)(vis >> (kb * 32 + 4 * half));
+}
+__device__ __forceinline__ bool bit_of(uint32_t w, int i) { return (w >> ((i >> 2) * 8 + (i & 3))) & 1u; }
+
+// Value of the other half of this lane's row combined with this one: lanes l and l+32 hold
+// the same query row.  v_permlane32_swap exchanges the two 32-lane halves between its two
+// operands; fed the same value twice, one result holds the low half's value and the other
+// the high half's in every lane, so a symmetric op of the two is the row-wide result
+// whichever way the swap goes.
+__device__ __forceinline__ float row_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Masked keys get score -inf (rare tiles only: partial cache tiles and tree tiles).
+__device__ __forceinline__ void mask_scores(f32x16 &s, uint32_t w) {
+#pragma unroll
+    for (int i = 0; i < 16; i++) s[i] = bit_of(w, i) ? s[i] : -INFINITY;
+}
+
+// c = scale * log2(e) is made positive once per workgroup (see normalise_scale), so the row
+// max of the raw scores gives the max of the scaled ones and -inf scores map to P = 0.
 struct SoftmaxRow {
     float m_ref;    // reference max (base-2 domain), -inf until the row sees a key
     float l;        // running sum of probabilities relative to m_ref (this lane's keys only)
-    float c;        // scale * log2(e)
+    float c;        // scale * log2(e), > 0
 
-    __device__ __forceinline__ Update update(const f32x16 &s, int kb, int half, bool need_mask, int nvalid,
-                                             uint64_t word) {
-        // extreme raw score in the direction of c (max for c >= 0), masked keys excluded
-        const bool neg = c < 0.f;
-        float e;
-        if (!neg) {
-            e = -INFINITY;
-            if (need_mask) {
+    __device__ __forceinline__ Update update(const f32x16 &s) {
+        float e = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 16; i++) e = fmaxf(e, key_visible(kb, i, half, nvalid, word) ? s[i] : -INFINITY);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; i++) e = fmaxf(e, s[i]);
-            }
-        } else {
-            e = INFINITY;
-#pragma unroll
-            for (int i = 0; i < 16; i++)
-                e = fminf(e, (!need_mask || key_visible(kb, i, half, nvalid, word)) ? s[i] : INFINITY);
-        }
-        const float o2 = __shfl_xor(e, 32);                    // the other half of the row
-        e = neg ? fminf(e, o2) : fmaxf(e, o2);
-        const bool any = neg ? (e != INFINITY) : (e != -INFINITY);
-        const float mx = any ? e * c : -INFINITY;
+        for (int i = 0; i < 16; i++) e = fmaxf(e, s[i]);
+        e = row_max(e);
+        const float mx = e * c;                                // -inf stays -inf
         const bool upd = mx > m_ref + kLazy;                   // also true for the first visible key
         const float m_new = upd ? mx : m_ref;
-        const float alpha = (upd && m_ref != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+        // exponent 0 (alpha = 1) unless an existing reference moves; no branch
+        const float alpha = __builtin_amdgcn_exp2f((upd && m_ref != -INFINITY) ? m_ref - m_new : 0.f);
         m_ref = m_new;
         return Update{m_new == -INFINITY ? 0.f : m_new, alpha};
     }
 
     // P = 2^(s*c - m) as bf16 hi + lo pairs (B operands of the two P.V MFMAs); returns sum P
-    __device__ __forceinline__ float probs(f32x16 &s, const Update &u, int kb, int half, bool need_mask, int nvalid,
-                                           uint64_t word, bf16x8 (&phi)[2], bf16x8 (&plo)[2]) const {
+    __device__ __forceinline__ float probs(const f32x16 &s, const Update &u, bf16x8 (&phi)[2],
+                                           bf16x8 (&plo)[2]) const {
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -u.m_use));
-            if (need_mask) p = key_visible(kb, i, half, nvalid, word) ? p : 0.f;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -u.m_use));
             sum += p;
             const __bf16 hi = (__bf16)p;
             phi[i >> 3][i & 7] = hi;
@@ -269,13 +299,11 @@ struct SoftmaxRow {
         return sum;
     }
 
-    __device__ __forceinline__ float probs_f32(f32x16 &s, const Update &u, int kb, int half, bool need_mask,
-                                               int nvalid, uint64_t word) const {
+    __device__ __forceinline__ float probs_f32(f32x16 &s, const Update &u) const {
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -u.m_use));
-            if (need_mask) p = key_visible(kb, i, half, nvalid, word) ? p : 0.f;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -u.m_use));
             s[i] = p;
             sum += p;
         }
@@ -284,48 +312,74 @@ struct SoftmaxRow {
 };
 
 // ------------------------------------------------------------------------------ MFMA blocks
+// sched_barrier mask that lets only VALU and SALU instructions move across it: the order of
+// LDS reads and MFMAs in the software pipelines below stays as written, while independent
+// softmax arithmetic can still be scheduled into the MFMA shadow.
+constexpr int kSchedAluOnly = 0x0002 | 0x0004;
 // The S^T chain keeps its accumulator in VGPRs (the softmax reads it with VALU ops) while the
 // 256 AGPRs hold O^T.  Compiler-selected MFMAs in a kernel that uses AGPRs all write AGPRs,
 // which would push part of O^T out, so these MFMAs are written out with explicit register
 // classes.  The wait states the compiler would insert are spelled out: 2 between dependent
 // 32x32x16 MFMAs on the same accumulator (s_nop 1), 12 or more before a VALU instruction
 // reads the result (s_nop 7 + s_nop 4 after the last one).  The first MFMA takes srcC = 0.
+template <int WAIT>
 __device__ __forceinline__ void mfma_s_first(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\ts_nop 1" : "=&v"(acc) : "v"(a), "v"(b));
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\ts_nop 1"
+                 : "=&v"(acc) : "v"(a), "v"(b), "i"(WAIT));
 }
+template <int WAIT>
 __device__ __forceinline__ void mfma_s_next(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 1" : "+v"(acc) : "v"(a), "v"(b));
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 1"
+                 : "+v"(acc) : "v"(a), "v"(b), "i"(WAIT));
 }
+template <int WAIT>
 __device__ __forceinline__ void mfma_s_last(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 4" : "+v"(acc) : "v"(a), "v"(b));
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 4"
+                 : "+v"(acc) : "v"(a), "v"(b), "i"(WAIT));
+}
+// K fragment read for the chain above.  Issued as asm so that the compiler does not add its
+// own (full) LDS wait in front of each asm MFMA; the MFMA that consumes the fragment waits
+// for it with an exact lgkmcnt.  LDS reads complete in order, so any LDS or scalar-memory
+// operation the compiler places in between only makes that count more conservative.
+template <int OFF>
+__device__ __forceinline__ void ds_read_k(bf16x8 &dst, const LDS_AS char *base) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(base), "i"(OFF));
 }
 
-// S^T for 32 keys (block kb of the tile) x this wave's 32 rows: NQ MFMA 32x32x16, with the
-// K fragments read from LDS QD steps ahead of the MFMA that consumes them.
-template <class Sh, int NQ>
-__device__ __forceinline__ f32x16 qk_block(const LDS_AS char *buf, int kb, const bf16x8 (&q)[NQ],
+// S^T for 32 keys (block KB of the tile) x this wave's 32 rows: NQ MFMA 32x32x16.  The K
+// fragment of step kk is read QD steps ahead into slot kk % (QD+1), so a slot is refilled
+// one MFMA after the one that last read it.
+template <class Sh, int NQ, int KB>
+__device__ __forceinline__ f32x16 qk_block(const LDS_AS char *buf, const bf16x8 (&q)[NQ],
                                            const int (&qk_base)[Sh::CB / 2]) {
     constexpr int PAT = Sh::CB / 2;
-    constexpr int QD = 6;
-    static_assert(NQ >= 2, "chain needs a first and a last MFMA");
+    constexpr int QD = NQ > 5 ? 5 : NQ - 1, NS = QD + 1;
+    static_assert(QD >= 1, "chain of at least two MFMAs");
     const LDS_AS char *pq[PAT];
 #pragma unroll
-    for (int j = 0; j < PAT; j++) pq[j] = buf + qk_base[j] + key_off<Sh>(kb * 32);
-    auto load = [&](int kk) { return *(const LDS_AS bf16x8 *)(pq[kk % PAT] + (kk / PAT) * 1024); };
-    bf16x8 kf[QD];
-#pragma unroll
-    for (int j = 0; j < QD && j < NQ; j++) kf[j] = load(j);
+    for (int j = 0; j < PAT; j++) pq[j] = buf + qk_base[j];
+    bf16x8 kf[NS];
+    static_for<0, QD>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        ds_read_k<key_off<Sh>(KB * 32) + (j / PAT) * 1024>(kf[j % NS], pq[j % PAT]);
+    });
     f32x16 acc;
-#pragma unroll
-    for (int kk = 0; kk < NQ; kk++) {
-        if (kk == 0)
-            mfma_s_first(acc, kf[0], q[0]);
-        else if (kk == NQ - 1)
-            mfma_s_last(acc, kf[kk % QD], q[kk]);
+    static_for<0, NQ>([&](auto KK) {
+        constexpr int kk = decltype(KK)::value;
+        // loads issued so far: steps < min(NQ, kk + QD); those after step kk may stay in flight
+        constexpr int issued = (kk + QD < NQ) ? kk + QD : NQ;
+        constexpr int after = issued - kk - 1;
+        if constexpr (kk == 0)
+            mfma_s_first<after>(acc, kf[0], q[0]);
+        else if constexpr (kk == NQ - 1)
+            mfma_s_last<after>(acc, kf[kk % NS], q[kk]);
         else
-            mfma_s_next(acc, kf[kk % QD], q[kk]);
-        if (kk + QD < NQ) kf[kk % QD] = load(kk + QD);
-    }
+            mfma_s_next<after>(acc, kf[kk % NS], q[kk]);
+        if constexpr (kk + QD < NQ) {
+            constexpr int n = kk + QD;
+            ds_read_k<key_off<Sh>(KB * 32) + (n / PAT) * 1024>(kf[n % NS], pq[n % PAT]);
+        }
+    });
     return acc;
 }
 
@@ -335,15 +389,15 @@ __device__ __forceinline__ f32x16 qk_block(const LDS_AS char *buf, int kb, const
 template <class Sh, int NT16>
 __device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const bf16x8 (&phi)[2],
                                          const bf16x8 (&plo)[2], f32x16 (&o)[NT16],
-                                         const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1]) {
+                                         const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1][2]) {
     constexpr int NSTEP = 2 * NT16;     // (h16, t16) pairs
     constexpr int PD = 4;
     auto load = [&](int st) {
         const int h16 = st / NT16, t16 = st % NT16;
         const int kbase = kb * 32 + 16 * h16;
-        const LDS_AS char *pv = buf + pv_base[(4 * t16 % Sh::CB) / 4] + (4 * t16 / Sh::CB) * 1024;
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(pv + key_off<Sh>(kbase)));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(pv + key_off<Sh>(kbase + 8)));
+        const int j = (4 * t16 % Sh::CB) / 4, cg_off = (4 * t16 / Sh::CB) * 1024 + key_off<Sh>(kbase);
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(buf + pv_base[j][0] + cg_off));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(buf + pv_base[j][1] + cg_off));
         return (bf16x8)__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     bf16x8 vf[PD];
@@ -351,6 +405,7 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const b
     for (int j = 0; j < PD; j++) vf[j] = load(j);
 #pragma unroll
     for (int st = 0; st < NSTEP; st += 2) {
+        __builtin_amdgcn_sched_barrier(kSchedAluOnly);
         const int h16 = st / NT16, t16 = st % NT16;
         o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], phi[h16], o[t16], 0, 0, 0);
         o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], phi[h16], o[t16 + 1], 0, 0, 0);
@@ -359,6 +414,7 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const b
         if (st + PD < NSTEP) vf[st % PD] = load(st + PD);
         if (st + 1 + PD < NSTEP) vf[(st + 1) % PD] = load(st + 1 + PD);
     }
+    __builtin_amdgcn_sched_barrier(kSchedAluOnly);
 }
 
 template <typename T, int DC, int DR>
@@ -429,23 +485,36 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
         }
     }
 
+    // Make c = scale*log2(e) positive: a negative scale negates the queries (exact: a sign
+    // flip), a zero scale zeroes them (every score is then exactly 0 as with scale 0) and
+    // uses c = 1.  Scores then order like scaled scores and masked -inf scores give P = 0.
+    float c_pos = a.scale_log2;
+    if (c_pos <= 0.f) {
+        const bool zero = c_pos == 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NQ; kk++) q[kk] = zero ? q[kk] * (T)0.f : -q[kk];
+        c_pos = zero ? 1.f : -c_pos;
+    }
+
     // per-lane LDS byte offsets (see lds_off) of the few swizzle patterns this lane reads
     constexpr int QK_PAT = Sh::CB / 2;                       // K reads: chunk 2kk + half
     constexpr int PV_PAT = Sh::CB >= 8 ? Sh::CB / 4 : 1;     // V^T reads: chunk 4*t16 + y
-    int qk_base[QK_PAT], pv_base[PV_PAT];
+    int qk_base[QK_PAT], pv_base[PV_PAT][2];
 #pragma unroll
     for (int j = 0; j < QK_PAT; j++) qk_base[j] = lds_off<Sh>(lane & 31, 2 * j + half);
     {
         const int w = 4 * half + ((lane & 15) >> 2);              // key within an 8-key group
         const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within 4 chunks (32 columns)
 #pragma unroll
-        for (int j = 0; j < PV_PAT; j++) pv_base[j] = lds_off<Sh>(w, 4 * j + y) + 8 * (lane & 1);
+        for (int j = 0; j < PV_PAT; j++)
+#pragma unroll
+            for (int e = 0; e < 2; e++) pv_base[j][e] = lds_off<Sh>(w + 8 * e, 4 * j + y) + 8 * (lane & 1);
     }
 
     f32x16 o[NT16];
 #pragma unroll
     for (int t = 0; t < NT16; t++) o[t] = (f32x16){};
-    SoftmaxRow sm{-INFINITY, 0.f, a.scale_log2};
+    SoftmaxRow sm{-INFINITY, 0.f, c_pos};
 
     for (int t = 0; t < n_tiles; t++) {
         wait_vm_all();
@@ -466,21 +535,24 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             word = a.masks[((int64_t)b * a.N + node) * a.W + tt];
         }
         const bool need_mask = is_tree || nvalid < kKeysPerTile;
+        const uint64_t vis = nvalid >= kKeysPerTile ? word : word & ((1ull << nvalid) - 1ull);
+        const uint32_t w0 = block_bits(vis, 0, half), w1 = block_bits(vis, 1, half);
 
         if constexpr (Sh::BF16) {
-            // Two 32-key halves.  The softmax VALU work of one half sits in the same basic
-            // block as MFMAs of the other (QK of half 1, then P.V of half 0), so it can issue
-            // while the matrix core is busy.
-            f32x16 s0 = qk_block<Sh, NQ>(buf, 0, q, qk_base);
-            const Update u0 = sm.update(s0, 0, half, need_mask, nvalid, word);
-            f32x16 s1 = qk_block<Sh, NQ>(buf, 1, q, qk_base);
+            // Two 32-key halves.  The softmax of half 1 sits in the same basic block as the
+            // P.V MFMAs of half 0, so its VALU work can issue while the matrix core is busy.
+            f32x16 s0 = qk_block<Sh, NQ, 0>(buf, q, qk_base);
+            if (need_mask) mask_scores(s0, w0);
+            const Update u0 = sm.update(s0);
             bf16x8 p0hi[2], p0lo[2];
-            const float l0 = sm.probs(s0, u0, 0, half, need_mask, nvalid, word, p0hi, p0lo);
+            const float l0 = sm.probs(s0, u0, p0hi, p0lo);
+            f32x16 s1 = qk_block<Sh, NQ, 1>(buf, q, qk_base);
+            if (need_mask) mask_scores(s1, w1);
             if (__ballot(u0.alpha != 1.f)) rescale_acc<NT16>(o, u0.alpha);
             pv_block<Sh, NT16>(buf, 0, p0hi, p0lo, o, pv_base);
-            const Update u1 = sm.update(s1, 1, half, need_mask, nvalid, word);
+            const Update u1 = sm.update(s1);
             bf16x8 p1hi[2], p1lo[2];
-            const float l1 = sm.probs(s1, u1, 1, half, need_mask, nvalid, word, p1hi, p1lo);
+            const float l1 = sm.probs(s1, u1, p1hi, p1lo);
             sm.l = (sm.l * u0.alpha + l0) * u1.alpha + l1;
             if (__ballot(u1.alpha != 1.f)) rescale_acc<NT16>(o, u1.alpha);
             pv_block<Sh, NT16>(buf, 1, p1hi, p1lo, o, pv_base);
@@ -495,8 +567,9 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
                         *(const LDS_AS float *)(buf + lds_off<Sh>(kb * 32 + (lane & 31), d >> 2) + ((d & 3) << 2));
                     sc = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, q[kk], sc, 0, 0, 0);
                 }
-                const Update u = sm.update(sc, kb, half, need_mask, nvalid, word);
-                const float lsum = sm.probs_f32(sc, u, kb, half, need_mask, nvalid, word);
+                if (need_mask) mask_scores(sc, kb ? w1 : w0);
+                const Update u = sm.update(sc);
+                const float lsum = sm.probs_f32(sc, u);
                 sm.l = sm.l * u.alpha + lsum;
                 if (__ballot(u.alpha != 1.f)) rescale_acc<NT16>(o, u.alpha);
 #pragma unroll
@@ -516,7 +589,7 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     const float m_run = sm.m_ref, l_run = sm.l;
 
     // ---- epilogue: lane holds O^T[dc = t16*32 + (i/4)*8 + 4*half + i%4][row]
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = row_sum(l_run);
     if (!row_ok) return;
     if (sb == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
