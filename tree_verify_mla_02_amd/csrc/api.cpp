@@ -89,6 +89,10 @@ int check_desc(const kdt_verify_desc *d) {
     for (const auto &x : s) {
         if (x.stride < x.width) return fail(KDT_ERR_INVALID_ARG, "%s = %lld is below the row width %d", x.name,
                                             (long long)x.stride, x.width);
+        // tile addressing uses 32-bit offsets over 64 rows
+        if (x.stride > (int64_t)(INT32_MAX / 128) / elem_size(d->dtype))
+            return fail(KDT_ERR_UNSUPPORTED, "%s = %lld is too large (row strides up to %d bytes)", x.name,
+                        (long long)x.stride, INT32_MAX / 128);
         if (x.stride % epc) return fail(KDT_ERR_MISALIGNED, "%s = %lld is not a multiple of %lld elements (16 bytes)",
                                         x.name, (long long)x.stride, (long long)epc);
     }
@@ -169,7 +173,9 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     if (S < 1) S = 1;
     x.nsplit = (int)S;
     x.chunk = chunk;
-    x.units = units0 * S;
+    // one group of RT units per (request, split); groups are dealt to 8 XCD lanes of the grid
+    const int64_t groups = (int64_t)d.batch * S;
+    x.units = (groups + 7) / 8 * 8 * rt;
     if (x.units > INT32_MAX) return false;
     const int64_t B = d.batch;
     size_t off = 0;
@@ -181,8 +187,8 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     x.off_header = take(sizeof(WsHeader));
     x.off_offsets = take(8 * B);
     x.off_lens = take(4 * B);
-    x.off_order = take(4 * B);
-    x.off_base = take(8 * (B + 1));
+    x.off_gwork = take(8 * (size_t)groups);
+    x.off_gorder = take(4 * (size_t)groups);
     x.off_units = take(16 * (size_t)x.units);
     if (S > 1) {
         x.off_ml = take(8 * (size_t)B * S * x.rows);
@@ -225,7 +231,7 @@ int kdt_build_visibility(const int32_t *parents, int32_t batch, int32_t num_node
         return fail(KDT_ERR_UNSUPPORTED, "num_nodes must be in [1, %d] (got %d)", kdt::kMaxNodes, num_nodes);
     if (((uintptr_t)parents & 3u) || ((uintptr_t)bitmask & 7u))
         return fail(KDT_ERR_MISALIGNED, "parents must be 4-byte and bitmask 8-byte aligned");
-    if ((int64_t)batch * num_nodes > (int64_t)INT32_MAX * 128) return fail(KDT_ERR_INVALID_ARG, "batch too large");
+    if (batch > INT32_MAX / 2) return fail(KDT_ERR_INVALID_ARG, "batch too large for one launch");
     const hipError_t e = kdt::launch_visibility(parents, batch, num_nodes, bitmask, dev_status, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "visibility launch");
     return ok();

@@ -58,21 +58,28 @@ __device__ __forceinline__ int splits_of(int L, int64_t chunk, int S) {
 }
 
 // ------------------------------------------------------------------------------ plan
-// One workgroup.  Validates cache_lens, writes per-request offsets (exclusive scan), a
-// longest-first order of requests and the unit list the attention grid reads: request by
-// request, and inside a request split-fastest, so that the units sharing one key split are
-// 8 apart in the grid and land on the same XCD (the dispatcher deals workgroups to the 8
-// XCDs round-robin); their key tiles are then read from one L2.
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ cache_lens, int B,
+// One workgroup.  Validates cache_lens, writes per-request offsets (exclusive scan) and the
+// unit list the attention grid reads.
+//
+// Unit order.  The dispatcher deals workgroups to the kXcds XCDs round-robin (grid slot u runs
+// on XCD u % kXcds), and each XCD has its own L2.  The row tiles of one (request, key split)
+// "group" all read the same key rows, so a group's units are given grid slots x + kXcds*k on
+// a single XCD x: its key tiles come from HBM once and from that L2 for the other row tiles.
+// Groups are sorted by work (keys), dealt to XCDs in snake order (0..7, 7..0, ...) to balance
+// the XCDs, and each XCD runs its groups longest first.
+constexpr int kXcds = 8;
+constexpr int kMaxSortGroups = 2048;    // above this the groups keep request order
+
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ cache_lens, int B, int N,
                                                     int64_t max_len, int64_t total_len, int RT, int S,
                                                     int64_t chunk, int64_t U, WsHeader *hdr,
-                                                    int64_t *offsets, int32_t *lens, int32_t *order,
-                                                    int64_t *base, int4 *units, int32_t *dev_status) {
+                                                    int64_t *offsets, int32_t *lens, int64_t *gwork,
+                                                    int32_t *gorder, int4 *units, int32_t *dev_status) {
     __shared__ int s_ok;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, nth = blockDim.x;
     if (tid == 0) s_ok = 1;
     __syncthreads();
-    for (int b = tid; b < B; b += blockDim.x) {
+    for (int b = tid; b < B; b += nth) {
         const int L = cache_lens[b];
         lens[b] = L;
         if (L < 0 || (int64_t)L > max_len) s_ok = 0;
@@ -85,46 +92,48 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
             off += lens[b] > 0 ? lens[b] : 0;
         }
         if (off > total_len) s_ok = 0;
+        hdr->ok = s_ok;
+        if (!s_ok && dev_status) atomicOr(dev_status, (int32_t)KDT_DEV_CACHE_LEN);
     }
     __syncthreads();
     const int ok = s_ok;
-    // rank = number of requests that go first: longer ones, then equal ones with lower index
-    for (int b = tid; b < B; b += blockDim.x) {
+    const int64_t G = (int64_t)B * S;
+    // work of group (b, s): its cache keys plus the tree keys for split 0; -1 = no such split
+    for (int64_t g = tid; g < G; g += nth) {
+        const int b = (int)(g / S), sp = (int)(g % S);
         const int L = lens[b];
-        int rank = 0;
-        for (int c = 0; c < B; c++) {
-            const int Lc = lens[c];
-            rank += (Lc > L) || (Lc == L && c < b);
+        int64_t w = -1;
+        if (ok && sp < splits_of(L, chunk, S)) {
+            const int64_t left = (int64_t)L - sp * chunk;
+            w = (left < chunk ? (left > 0 ? left : 0) : chunk) + (sp == 0 ? N : 0);
         }
-        order[rank] = b;
+        gwork[g] = w;
     }
+    for (int64_t u = tid; u < U; u += nth) units[u] = make_int4(-1, 0, 0, 0);
     __syncthreads();
-    if (tid == 0) {
-        int64_t acc = 0;
-        for (int p = 0; p < B; p++) {
-            base[p] = acc;
-            acc += (int64_t)RT * (ok ? splits_of(lens[order[p]], chunk, S) : 0);
-        }
-        base[B] = acc;
-        hdr->ok = ok;
-        if (!ok && dev_status) atomicOr(dev_status, (int32_t)KDT_DEV_CACHE_LEN);
-    }
-    __syncthreads();
-    const int64_t used = base[B];
-    for (int64_t u = tid; u < U; u += blockDim.x) {
-        int4 d = make_int4(-1, 0, 0, 0);
-        if (u < used) {
-            int lo = 0, hi = B - 1;          // last p with base[p] <= u
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (base[mid] <= u) lo = mid; else hi = mid - 1;
+    for (int64_t g = tid; g < G; g += nth) {
+        int64_t rank = g;
+        if (G <= kMaxSortGroups) {      // more work first, ties by index
+            const int64_t w = gwork[g];
+            rank = 0;
+            for (int64_t h = 0; h < G; h++) {
+                const int64_t wh = gwork[h];
+                rank += (wh > w) || (wh == w && h < g);
             }
-            const int b = order[lo];
-            const int sb = splits_of(lens[b], chunk, S);
-            const int64_t v = u - base[lo];
-            d = make_int4(b, (int)(v / sb), (int)(v % sb), sb);
         }
-        units[u] = d;
+        gorder[rank] = (int32_t)g;
+    }
+    __syncthreads();
+    for (int64_t e = tid; e < G * RT; e += nth) {
+        const int64_t p = e / RT;
+        const int rt = (int)(e % RT);
+        const int g = gorder[p];
+        if (gwork[g] < 0) continue;
+        const int64_t round = p / kXcds;
+        const int j = (int)(p % kXcds);
+        const int x = (round & 1) ? kXcds - 1 - j : j;
+        const int b = g / S, sp = g % S;
+        units[x + kXcds * (round * RT + rt)] = make_int4(b, rt, sp, splits_of(lens[b], chunk, S));
     }
 }
 
@@ -174,29 +183,65 @@ __host__ __device__ constexpr int key_off(int k) {
     return (k / Sh::KB) * Sh::NCG * 1024 + (k % Sh::KB) * Sh::CB * 16;
 }
 
-// Issue this wave's share of one 64-key tile: rows row0 .. row0+63 of (lat | rope), keys at
-// or beyond nvalid re-read the last valid row (their scores are masked; the data only has
-// to be finite).  Lane l fills 16-byte slot l of a 1 KB block.
+// One 16-byte-per-lane HBM -> LDS copy (lane l writes bytes 16l..16l+15 at lds_addr).  It
+// is issued as asm: as a compiler intrinsic it counts as an LDS store of unknown address, and
+// the compiler then waits for it (vmcnt) before every later LDS read -- a full memory latency
+// after each batch of copies.  The copies only ever target the tile buffer that is not being
+// read, and the wait that makes them visible is explicit (s_waitcnt vmcnt(0) + barrier at the
+// top of the next tile).
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "m0");
+}
+
+// HBM -> LDS copy of one 64-key tile, issued by every wave in parts so that the
+// global_load_lds instructions fall between MFMAs instead of in one burst.  Lane l fills
+// 16-byte slot l of a 1 KB block; a wave owns key groups wave, wave+4, ...  Addresses are a
+// wave-uniform base (the tile's first key row) plus a 32-bit per-lane offset computed once
+// per tile, so each load is one instruction with an immediate chunk offset.  Keys at or
+// beyond `nvalid` re-read the last valid row (their scores are masked; the data only has to
+// be finite).
 template <class Sh, typename T>
-__device__ __forceinline__ void issue_tile(LDS_AS char *buf, const T *__restrict__ lat, int64_t lat_stride,
-                                           const T *__restrict__ rope, int64_t rope_stride, int64_t row0,
-                                           int nvalid, int wave, int lane) {
-    const int kr = lane / Sh::CB;
-    for (int kg = wave; kg < Sh::NKG; kg += kWaves) {
-        const int slot_key = kg * Sh::KB + kr;                    // the key this LDS slot holds
-        const int cc = (lane % Sh::CB) ^ Sh::swz(slot_key);      // its logical chunk
-        const int key = slot_key < nvalid ? slot_key : nvalid - 1;
-        const T *lrow = lat + (row0 + key) * lat_stride;
-        const T *rrow = rope + (row0 + key) * rope_stride;
+struct TileDma {
+    static constexpr int KGW = (Sh::NKG + kWaves - 1) / kWaves;   // key groups per wave (max)
+    static constexpr int NINST = KGW * Sh::NCG;                     // loads per wave per tile
+    const char *lat, *rope;      // wave-uniform bases: key row 0 of the tile
+    LDS_AS char *dst;            // the tile buffer
+    int off_lat[KGW], off_rope[KGW];
+    int wave;
+
+    __device__ __forceinline__ void setup(LDS_AS char *buf, const T *lat_base, int64_t lat_stride,
+                                          const T *rope_base, int64_t rope_stride, int64_t row0, int nvalid,
+                                          int wave_, int lane) {
+        wave = wave_;
+        dst = buf;
+        lat = (const char *)(lat_base + row0 * lat_stride);
+        rope = (const char *)(rope_base + row0 * rope_stride);
+        const int kr = lane / Sh::CB;
 #pragma unroll
-        for (int cg = 0; cg < Sh::NCG; cg++) {
-            const int c = cg * Sh::CB + cc;
-            const T *src = (cg * Sh::CB < Sh::CH_LAT) ? lrow + c * Sh::EPC : rrow + (c - Sh::CH_LAT) * Sh::EPC;
-            __builtin_amdgcn_global_load_lds((const void *)src,
-                                             (LDS_AS void *)(buf + ((kg * Sh::NCG + cg) << 10)), 16, 0, 0);
+        for (int g = 0; g < KGW; g++) {
+            const int slot_key = (wave + kWaves * g) * Sh::KB + kr;    // the key this LDS slot holds
+            const int cc = (lane % Sh::CB) ^ Sh::swz(slot_key);        // its logical chunk in the group
+            const int key = slot_key < nvalid ? slot_key : nvalid - 1;
+            off_lat[g] = key * (int)(lat_stride * (int64_t)sizeof(T)) + cc * 16;
+            off_rope[g] = key * (int)(rope_stride * (int64_t)sizeof(T)) + cc * 16;
         }
     }
-}
+
+    // loads [J0, J1) of this wave's NINST (key group major, chunk group minor)
+    template <int J0, int J1>
+    __device__ __forceinline__ void issue() const {
+        static_for<J0, (J1 < NINST ? J1 : NINST)>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            constexpr int g = j / Sh::NCG, cg = j % Sh::NCG;
+            const int kg = wave + kWaves * g;
+            if (kg < Sh::NKG) {
+                const char *src = (cg * Sh::CB < Sh::CH_LAT) ? lat + off_lat[g] + cg * Sh::CB * 16
+                                                             : rope + off_rope[g] + (cg * Sh::CB - Sh::CH_LAT) * 16;
+                lds_dma16(src, (uint32_t)(uintptr_t)(dst + ((kg * Sh::NCG + cg) << 10)));
+            }
+        });
+    }
+};
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -270,11 +315,7 @@ struct SoftmaxRow {
     float l;        // running sum of probabilities relative to m_ref (this lane's keys only)
     float c;        // scale * log2(e), > 0
 
-    __device__ __forceinline__ Update update(const f32x16 &s) {
-        float e = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; i++) e = fmaxf(e, s[i]);
-        e = row_max(e);
+    __device__ __forceinline__ Update update_from_max(float e) {
         const float mx = e * c;                                // -inf stays -inf
         const bool upd = mx > m_ref + kLazy;                   // also true for the first visible key
         const float m_new = upd ? mx : m_ref;
@@ -282,6 +323,13 @@ struct SoftmaxRow {
         const float alpha = __builtin_amdgcn_exp2f((upd && m_ref != -INFINITY) ? m_ref - m_new : 0.f);
         m_ref = m_new;
         return Update{m_new == -INFINITY ? 0.f : m_new, alpha};
+    }
+
+    __device__ __forceinline__ Update update(const f32x16 &s) {
+        float e = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; i++) e = fmaxf(e, s[i]);
+        return update_from_max(row_max(e));
     }
 
     // P = 2^(s*c - m) as bf16 hi + lo pairs (B operands of the two P.V MFMAs); returns sum P
@@ -309,6 +357,69 @@ struct SoftmaxRow {
         }
         return sum;
     }
+};
+
+// The softmax of one 32-key block cut into kSmStages steps, so that an MFMA pipeline can
+// issue one step between two of its MFMAs (the matrix core then works while the VALU does):
+// 8 partial maxima, the row update (cross-lane max, reference, rescale factor), and 8 pairs of
+// probabilities converted to bf16 hi + lo.
+constexpr int kSmStages = 17;
+struct BlockSm {
+    f32x16 s;          // raw scores (masked keys -inf)
+    float e;           // partial max
+    float sum;         // sum of this lane's probabilities
+    Update u;
+    bf16x8 phi[2], plo[2];
+
+    template <int ST>
+    __device__ __forceinline__ void stage(SoftmaxRow &sm) {
+        if constexpr (ST == 0) {
+            e = fmaxf(s[0], s[1]);
+        } else if constexpr (ST < 8) {
+            e = fmaxf(e, fmaxf(s[2 * ST], s[2 * ST + 1]));
+        } else if constexpr (ST == 8) {
+            u = sm.update_from_max(row_max(e));
+            sum = 0.f;
+        } else if constexpr (ST < kSmStages) {
+            constexpr int i = 2 * (ST - 9);
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sm.c, -u.m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], sm.c, -u.m_use));
+            sum += p0;
+            sum += p1;
+            const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+            phi[i >> 3][i & 7] = h0;
+            phi[i >> 3][(i + 1) & 7] = h1;
+            plo[i >> 3][i & 7] = (__bf16)(p0 - (float)h0);
+            plo[i >> 3][(i + 1) & 7] = (__bf16)(p1 - (float)h1);
+        }
+    }
+};
+
+// Compile-time placement of items [LO, HI) into the steps of a pipeline: item LO + n goes to
+// step FIRST + n*EVERY.  `at<K, NSTEPS>` runs the item placed at step K; `tail<NSTEPS>` runs,
+// in order, the items whose step would be NSTEPS or later, so every item runs exactly once
+// and in order whatever the pipeline length.
+template <int LO, int HI, int FIRST, int EVERY>
+struct Spread {
+    static constexpr int step_of(int n) { return FIRST + n * EVERY; }
+    template <int K, int NSTEPS, class F>
+    __device__ __forceinline__ static void at(F &&f) {
+        constexpr int rel = K - FIRST;
+        if constexpr (K < NSTEPS && rel >= 0 && rel % EVERY == 0 && LO + rel / EVERY < HI)
+            f(IntC<LO + rel / EVERY>{});
+    }
+    template <int NSTEPS, class F>
+    __device__ __forceinline__ static void tail(F &&f) {
+        static_for<LO, HI>([&](auto J) {
+            constexpr int n = decltype(J)::value - LO;
+            if constexpr (step_of(n) >= NSTEPS) f(J);
+        });
+    }
+};
+
+struct NoFill {
+    template <class K>
+    __device__ __forceinline__ void operator()(K) const {}
 };
 
 // ------------------------------------------------------------------------------ MFMA blocks
@@ -349,9 +460,9 @@ __device__ __forceinline__ void ds_read_k(bf16x8 &dst, const LDS_AS char *base) 
 // S^T for 32 keys (block KB of the tile) x this wave's 32 rows: NQ MFMA 32x32x16.  The K
 // fragment of step kk is read QD steps ahead into slot kk % (QD+1), so a slot is refilled
 // one MFMA after the one that last read it.
-template <class Sh, int NQ, int KB>
+template <class Sh, int NQ, int KB, class F>
 __device__ __forceinline__ f32x16 qk_block(const LDS_AS char *buf, const bf16x8 (&q)[NQ],
-                                           const int (&qk_base)[Sh::CB / 2]) {
+                                           const int (&qk_base)[Sh::CB / 2], F &&fill) {
     constexpr int PAT = Sh::CB / 2;
     constexpr int QD = NQ > 5 ? 5 : NQ - 1, NS = QD + 1;
     static_assert(QD >= 1, "chain of at least two MFMAs");
@@ -379,6 +490,8 @@ __device__ __forceinline__ f32x16 qk_block(const LDS_AS char *buf, const bf16x8 
             constexpr int n = kk + QD;
             ds_read_k<key_off<Sh>(KB * 32) + (n / PAT) * 1024>(kf[n % NS], pq[n % PAT]);
         }
+        fill(KK);                                  // independent work for the MFMA shadow
+        __builtin_amdgcn_sched_barrier(0);         // keep each step's instructions together
     });
     return acc;
 }
@@ -386,10 +499,10 @@ __device__ __forceinline__ f32x16 qk_block(const LDS_AS char *buf, const bf16x8 
 // O^T += V^T P^T for 32 keys (block kb): for each 16-key step and 32-column tile, one V^T
 // fragment (two ds_read_b64_tr_b16) feeds the hi and the lo MFMA.  Fragments are read kPD
 // steps ahead; column tiles go in pairs so consecutive MFMAs use different accumulators.
-template <class Sh, int NT16>
+template <class Sh, int NT16, class F>
 __device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const bf16x8 (&phi)[2],
                                          const bf16x8 (&plo)[2], f32x16 (&o)[NT16],
-                                         const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1][2]) {
+                                         const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1][2], F &&fill) {
     constexpr int NSTEP = 2 * NT16;     // (h16, t16) pairs
     constexpr int PD = 4;
     auto load = [&](int st) {
@@ -403,18 +516,19 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const b
     bf16x8 vf[PD];
 #pragma unroll
     for (int j = 0; j < PD; j++) vf[j] = load(j);
-#pragma unroll
-    for (int st = 0; st < NSTEP; st += 2) {
-        __builtin_amdgcn_sched_barrier(kSchedAluOnly);
-        const int h16 = st / NT16, t16 = st % NT16;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NSTEP / 2>([&](auto S2) {
+        constexpr int st = 2 * decltype(S2)::value;
+        constexpr int h16 = st / NT16, t16 = st % NT16;
         o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], phi[h16], o[t16], 0, 0, 0);
         o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], phi[h16], o[t16 + 1], 0, 0, 0);
         o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], plo[h16], o[t16], 0, 0, 0);
         o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], plo[h16], o[t16 + 1], 0, 0, 0);
-        if (st + PD < NSTEP) vf[st % PD] = load(st + PD);
-        if (st + 1 + PD < NSTEP) vf[(st + 1) % PD] = load(st + 1 + PD);
-    }
-    __builtin_amdgcn_sched_barrier(kSchedAluOnly);
+        if constexpr (st + PD < NSTEP) vf[st % PD] = load(st + PD);
+        if constexpr (st + 1 + PD < NSTEP) vf[(st + 1) % PD] = load(st + 1 + PD);
+        fill(S2);                                  // independent work for the MFMA shadow
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 template <typename T, int DC, int DR>
@@ -429,7 +543,8 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     const int4 unit = a.units[blockIdx.x];
     if (unit.x < 0) return;
     const int b = unit.x, rt = unit.y, s = unit.z, sb = unit.w;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps LDS bases in SGPRs
     const int half = lane >> 5;                          // 0: lanes 0-31, 1: lanes 32-63
     const int64_t R = a.R;
 
@@ -450,22 +565,27 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     const int n_tiles = n_cache + n_tree;
     const int64_t cache_row0 = a.offsets[b] + k0;
 
-    auto issue = [&](int t) {
+    using Dma = TileDma<Sh, T>;
+    auto dma_setup = [&](Dma &d, int t) {
         LDS_AS char *buf = (LDS_AS char *)smem + (t & 1) * Sh::TILE_BYTES;
         if (t < n_cache) {
-            const int64_t row0 = cache_row0 + (int64_t)t * kKeysPerTile;
             const int64_t left = k1 - k0 - (int64_t)t * kKeysPerTile;
-            issue_tile<Sh, T>(buf, (const T *)a.ckv, a.ckv_stride, (const T *)a.krope, a.krope_stride, row0,
-                              left < kKeysPerTile ? (int)left : kKeysPerTile, wave, lane);
+            d.setup(buf, (const T *)a.ckv, a.ckv_stride, (const T *)a.krope, a.krope_stride,
+                    cache_row0 + (int64_t)t * kKeysPerTile, left < kKeysPerTile ? (int)left : kKeysPerTile, wave,
+                    lane);
         } else {
             const int tt = t - n_cache;
             const int left = a.N - tt * kKeysPerTile;
-            issue_tile<Sh, T>(buf, (const T *)a.tckv, a.tckv_stride, (const T *)a.tkrope, a.tkrope_stride,
-                              (int64_t)b * a.N + (int64_t)tt * kKeysPerTile,
-                              left < kKeysPerTile ? left : kKeysPerTile, wave, lane);
+            d.setup(buf, (const T *)a.tckv, a.tckv_stride, (const T *)a.tkrope, a.tkrope_stride,
+                    (int64_t)b * a.N + (int64_t)tt * kKeysPerTile, left < kKeysPerTile ? left : kKeysPerTile, wave,
+                    lane);
         }
     };
-    issue(0);
+    {
+        Dma d0;
+        dma_setup(d0, 0);
+        d0.template issue<0, Dma::NINST>();
+    }
 
     // ---- queries to registers: B operand of S^T = K Q^T
     typedef typename std::conditional<Sh::BF16, bf16x8, float>::type QFrag;
@@ -519,44 +639,81 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     for (int t = 0; t < n_tiles; t++) {
         wait_vm_all();
         __syncthreads();                 // tile t is in LDS; every wave is done with tile t-1
-        if (t + 1 < n_tiles) issue(t + 1);
         const LDS_AS char *buf = (const LDS_AS char *)smem + (t & 1) * Sh::TILE_BYTES;
 
-        // ---- which keys of this tile the row sees: a full cache tile needs no mask
+        // ---- which keys of this tile the row sees: a full cache tile needs no mask.  The tree
+        // tile's ancestor word is loaded and consumed here, before any copy of tile t+1 is
+        // issued: a later first use would make its vmcnt wait cover those copies as well.
         const bool is_tree = t >= n_cache;
-        int nvalid;
-        uint64_t word = ~0ull;
+        bool need_mask;
+        uint32_t w0 = ~0u, w1 = ~0u;
         if (!is_tree) {
             const int64_t left = k1 - k0 - (int64_t)t * kKeysPerTile;
-            nvalid = left < kKeysPerTile ? (int)left : kKeysPerTile;
+            need_mask = left < kKeysPerTile;
+            if (need_mask) {
+                const uint64_t vis = (1ull << left) - 1ull;
+                w0 = block_bits(vis, 0, half);
+                w1 = block_bits(vis, 1, half);
+            }
         } else {
             const int tt = t - n_cache;
-            nvalid = a.N - tt * kKeysPerTile;
-            word = a.masks[((int64_t)b * a.N + node) * a.W + tt];
+            const int nvalid = a.N - tt * kKeysPerTile;
+            uint64_t vis = a.masks[((int64_t)b * a.N + node) * a.W + tt];
+            if (nvalid < kKeysPerTile) vis &= (1ull << nvalid) - 1ull;
+            w0 = block_bits(vis, 0, half);
+            w1 = block_bits(vis, 1, half);
+            need_mask = true;
         }
-        const bool need_mask = is_tree || nvalid < kKeysPerTile;
-        const uint64_t vis = nvalid >= kKeysPerTile ? word : word & ((1ull << nvalid) - 1ull);
-        const uint32_t w0 = block_bits(vis, 0, half), w1 = block_bits(vis, 1, half);
+        __builtin_amdgcn_sched_barrier(0);
+        // tile t+1 goes into the other buffer, its loads spread over this tile's MFMA chains
+        const bool more = t + 1 < n_tiles;
+        Dma dn;
+        if (more) dma_setup(dn, t + 1);
+        constexpr int P1 = Dma::NINST / 4, P2 = Dma::NINST / 2, P3 = 3 * Dma::NINST / 4;
+        if constexpr (!Sh::BF16)
+            if (more) dn.template issue<0, P1>();
 
         if constexpr (Sh::BF16) {
-            // Two 32-key halves.  The softmax of half 1 sits in the same basic block as the
-            // P.V MFMAs of half 0, so its VALU work can issue while the matrix core is busy.
-            f32x16 s0 = qk_block<Sh, NQ, 0>(buf, q, qk_base);
-            if (need_mask) mask_scores(s0, w0);
-            const Update u0 = sm.update(s0);
-            bf16x8 p0hi[2], p0lo[2];
-            const float l0 = sm.probs(s0, u0, p0hi, p0lo);
-            f32x16 s1 = qk_block<Sh, NQ, 1>(buf, q, qk_base);
-            if (need_mask) mask_scores(s1, w1);
-            if (__ballot(u0.alpha != 1.f)) rescale_acc<NT16>(o, u0.alpha);
-            pv_block<Sh, NT16>(buf, 0, p0hi, p0lo, o, pv_base);
-            const Update u1 = sm.update(s1);
-            bf16x8 p1hi[2], p1lo[2];
-            const float l1 = sm.probs(s1, u1, p1hi, p1lo);
-            sm.l = (sm.l * u0.alpha + l0) * u1.alpha + l1;
-            if (__ballot(u1.alpha != 1.f)) rescale_acc<NT16>(o, u1.alpha);
-            pv_block<Sh, NT16>(buf, 1, p1hi, p1lo, o, pv_base);
+            // Two 32-key halves.  Block 0: QK, then its softmax stages are interleaved with
+            // block 1's QK chain.  Block 1's softmax follows block 0's P.V chain.  The copy of
+            // tile t+1 is spread over the four chains; work a chain is too short to hold is done
+            // right after it (Spread::tail).
+            constexpr int NPV = NT16;                       // P.V steps per block (4 MFMAs each)
+            BlockSm b0, b1;
+            using D0 = Spread<0, P1, 4, 1>;                 // loads [0, P1) at QK0 steps 4, 5, ...
+            b0.s = qk_block<Sh, NQ, 0>(buf, q, qk_base, [&](auto K) {
+                if (more) D0::template at<decltype(K)::value, NQ>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            });
+            if (more) D0::template tail<NQ>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            if (need_mask) mask_scores(b0.s, w0);
+            using S0 = Spread<0, kSmStages, 0, 2>;          // softmax of block 0 at QK1 steps 0, 2, 4, ...
+            using D1 = Spread<P1, P2, 1, 2>;                // loads [P1, P2) at QK1 steps 1, 3, ...
+            b1.s = qk_block<Sh, NQ, 1>(buf, q, qk_base, [&](auto K) {
+                constexpr int k = decltype(K)::value;
+                S0::template at<k, NQ>([&](auto J) { b0.template stage<J.value>(sm); });
+                if (more) D1::template at<k, NQ>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            });
+            S0::template tail<NQ>([&](auto J) { b0.template stage<J.value>(sm); });
+            if (more) D1::template tail<NQ>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            if (need_mask) mask_scores(b1.s, w1);
+            if (__ballot(b0.u.alpha != 1.f)) rescale_acc<NT16>(o, b0.u.alpha);
+            // Block 1's softmax runs after block 0's P.V chain rather than inside it: placed
+            // inside, its VALU work lengthened the chain more than it saved.
+            using D2 = Spread<P2, P3, 0, 1>;
+            pv_block<Sh, NT16>(buf, 0, b0.phi, b0.plo, o, pv_base, [&](auto K) {
+                if (more) D2::template at<decltype(K)::value, NPV>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            });
+            if (more) D2::template tail<NPV>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            static_for<0, kSmStages>([&](auto J) { b1.template stage<J.value>(sm); });
+            sm.l = (sm.l * b0.u.alpha + b0.sum) * b1.u.alpha + b1.sum;
+            if (__ballot(b1.u.alpha != 1.f)) rescale_acc<NT16>(o, b1.u.alpha);
+            using D3 = Spread<P3, Dma::NINST, 0, 1>;
+            pv_block<Sh, NT16>(buf, 1, b1.phi, b1.plo, o, pv_base, [&](auto K) {
+                if (more) D3::template at<decltype(K)::value, NPV>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            });
+            if (more) D3::template tail<NPV>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
         } else {
+            if (more) dn.template issue<P1, Dma::NINST>();
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
                 f32x16 sc = (f32x16){};
@@ -659,10 +816,10 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 hipError_t launch_plan(const int32_t *cache_lens, const kdt_verify_desc &d, const Geometry &g, void *ws,
                        int32_t *dev_status, hipStream_t st) {
     char *w = (char *)ws;
-    plan_kernel<<<1, 1024, 0, st>>>(cache_lens, d.batch, d.max_cache_len, d.total_cache_len, g.row_tiles,
-                                    g.nsplit, g.chunk, g.units, (WsHeader *)(w + g.off_header),
+    plan_kernel<<<1, 1024, 0, st>>>(cache_lens, d.batch, d.num_nodes, d.max_cache_len, d.total_cache_len,
+                                    g.row_tiles, g.nsplit, g.chunk, g.units, (WsHeader *)(w + g.off_header),
                                     (int64_t *)(w + g.off_offsets), (int32_t *)(w + g.off_lens),
-                                    (int32_t *)(w + g.off_order), (int64_t *)(w + g.off_base),
+                                    (int64_t *)(w + g.off_gwork), (int32_t *)(w + g.off_gorder),
                                     (int4 *)(w + g.off_units), dev_status);
     return hipGetLastError();
 }
