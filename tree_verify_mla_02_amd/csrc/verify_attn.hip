@@ -34,7 +34,10 @@ namespace kdt {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 template <int I>
@@ -183,30 +186,33 @@ __host__ __device__ constexpr int key_off(int k) {
     return (k / Sh::KB) * Sh::NCG * 1024 + (k % Sh::KB) * Sh::CB * 16;
 }
 
-// One 16-byte-per-lane HBM -> LDS copy (lane l writes bytes 16l..16l+15 at lds_addr).  It
-// is issued as asm: as a compiler intrinsic it counts as an LDS store of unknown address, and
-// the compiler then waits for it (vmcnt) before every later LDS read -- a full memory latency
+// One 16-byte-per-lane HBM -> LDS copy (lane l writes bytes 16l..16l+15 at lds_addr) from
+// base + voff, with base a wave-uniform 64-bit pointer in SGPRs and voff this lane's 32-bit
+// byte offset (the global "saddr" form: no 64-bit address arithmetic per copy in VALU).  The
+// instruction's immediate offset is left at 0: for LDS-DMA loads it also moves the LDS
+// destination, so the per-chunk offset goes into the scalar base instead.  The copy is issued
+// as asm: as a compiler intrinsic it counts as an LDS store of unknown address, and the
+// compiler then waits for it (vmcnt) before every later LDS read -- a full memory latency
 // after each batch of copies.  The copies only ever target the tile buffer that is not being
 // read, and the wait that makes them visible is explicit (s_waitcnt vmcnt(0) + barrier at the
 // top of the next tile).
-__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "m0");
+__device__ __forceinline__ void lds_dma16(const char *base, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 : : "v"(voff), "s"(base), "s"(lds_addr) : "m0");
 }
 
-// HBM -> LDS copy of one 64-key tile, issued by every wave in parts so that the
-// global_load_lds instructions fall between MFMAs instead of in one burst.  Lane l fills
-// 16-byte slot l of a 1 KB block; a wave owns key groups wave, wave+4, ...  Addresses are a
-// wave-uniform base (the tile's first key row) plus a 32-bit per-lane offset computed once
-// per tile, so each load is one instruction with an immediate chunk offset.  Keys at or
-// beyond `nvalid` re-read the last valid row (their scores are masked; the data only has to
-// be finite).
+// Copy of one key tile (kKeysPerTile rows of D elements, latent and rope parts from separate
+// bases) into the LDS layout of lds_off.  Each copy moves a 1 KB block: KB keys x CB chunks,
+// lane -> (key kr = lane / CB, stored chunk lane % CB), so the swizzle is applied by choosing
+// which logical chunk of the row a lane fetches.  Keys past the end of a partial tile re-read
+// the last valid row (their scores are masked).  Wave w copies key groups w, w + 4, ...
 template <class Sh, typename T>
 struct TileDma {
     static constexpr int KGW = (Sh::NKG + kWaves - 1) / kWaves;   // key groups per wave (max)
     static constexpr int NINST = KGW * Sh::NCG;                     // loads per wave per tile
     const char *lat, *rope;      // wave-uniform bases: key row 0 of the tile
     LDS_AS char *dst;            // the tile buffer
-    int off_lat[KGW], off_rope[KGW];
+    uint32_t off_lat[KGW], off_rope[KGW];
     int wave;
 
     __device__ __forceinline__ void setup(LDS_AS char *buf, const T *lat_base, int64_t lat_stride,
@@ -217,13 +223,15 @@ struct TileDma {
         lat = (const char *)(lat_base + row0 * lat_stride);
         rope = (const char *)(rope_base + row0 * rope_stride);
         const int kr = lane / Sh::CB;
+        const uint32_t lsb = (uint32_t)(lat_stride * (int64_t)sizeof(T));
+        const uint32_t rsb = (uint32_t)(rope_stride * (int64_t)sizeof(T));
 #pragma unroll
         for (int g = 0; g < KGW; g++) {
             const int slot_key = (wave + kWaves * g) * Sh::KB + kr;    // the key this LDS slot holds
-            const int cc = (lane % Sh::CB) ^ Sh::swz(slot_key);        // its logical chunk in the group
-            const int key = slot_key < nvalid ? slot_key : nvalid - 1;
-            off_lat[g] = key * (int)(lat_stride * (int64_t)sizeof(T)) + cc * 16;
-            off_rope[g] = key * (int)(rope_stride * (int64_t)sizeof(T)) + cc * 16;
+            const uint32_t cc = (uint32_t)((lane % Sh::CB) ^ Sh::swz(slot_key));   // its logical chunk
+            const uint32_t key = (uint32_t)(slot_key < nvalid ? slot_key : nvalid - 1);
+            off_lat[g] = key * lsb + cc * 16u;
+            off_rope[g] = key * rsb + cc * 16u;
         }
     }
 
@@ -234,10 +242,13 @@ struct TileDma {
             constexpr int j = decltype(J)::value;
             constexpr int g = j / Sh::NCG, cg = j % Sh::NCG;
             const int kg = wave + kWaves * g;
-            if (kg < Sh::NKG) {
-                const char *src = (cg * Sh::CB < Sh::CH_LAT) ? lat + off_lat[g] + cg * Sh::CB * 16
-                                                             : rope + off_rope[g] + (cg * Sh::CB - Sh::CH_LAT) * 16;
-                lds_dma16(src, (uint32_t)(uintptr_t)(dst + ((kg * Sh::NCG + cg) << 10)));
+            // every wave has KGW groups when they divide evenly: no test (and no branch)
+            if (Sh::NKG % kWaves == 0 || kg < Sh::NKG) {
+                const uint32_t lds = (uint32_t)(uintptr_t)(dst + ((kg * Sh::NCG + cg) << 10));
+                if constexpr (cg * Sh::CB < Sh::CH_LAT)
+                    lds_dma16(lat + cg * Sh::CB * 16, off_lat[g], lds);
+                else
+                    lds_dma16(rope + (cg * Sh::CB - Sh::CH_LAT) * 16, off_rope[g], lds);
             }
         });
     }
@@ -359,38 +370,89 @@ struct SoftmaxRow {
     }
 };
 
-// The softmax of one 32-key block cut into kSmStages steps, so that an MFMA pipeline can
-// issue one step between two of its MFMAs (the matrix core then works while the VALU does):
-// 8 partial maxima, the row update (cross-lane max, reference, rescale factor), and 8 pairs of
-// probabilities converted to bf16 hi + lo.
-constexpr int kSmStages = 17;
+// The softmax of one 32-key block cut into kSmStages micro-steps of at most four VALU
+// instructions (an exp counts double), so that an MFMA pipeline can issue one of them after
+// each MFMA.  A wave issues in order and an MFMA holds the issue port for about half of its 32
+// cycles, so only work placed between two MFMAs runs in the matrix core's shadow: a larger
+// group stalls the next MFMA.  Steps: partial maxima (4), cross-lane max and reference update
+// (3), then per pair of probabilities (8 pairs) exp2, sum, and the exact split into bf16 hi +
+// lo (4 each): p = hi + lo_exact with hi = bf16(p) (round to nearest) and lo_exact = p - hi
+// exact in fp32, then lo = bf16(lo_exact).
+constexpr int kSmPre = 7;
+constexpr int kSmStages = kSmPre + 8 * 4;
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+// Empty asm that takes a value as an in/out operand: the value must be computed at this point
+// of the program.  Without it the compiler sinks the softmax arithmetic towards its later uses
+// (the next P.V chain), out of the MFMA shadow it was placed in.
+template <typename V>
+__device__ __forceinline__ void pin(V &x) { asm volatile("" : "+v"(x)); }
+
 struct BlockSm {
     f32x16 s;          // raw scores (masked keys -inf)
-    float e;           // partial max
+    float m0, m1, m2, m3, m4;   // partial maxima
+    float mx;          // new reference candidate
     float sum;         // sum of this lane's probabilities
     Update u;
-    bf16x8 phi[2], plo[2];
+    float x1, p0, p1, h0f;
+    uint32_t hp;
+    u32x4 phi[2], plo[2];   // P as bf16 pairs: dword k of phi[h] holds keys 8h + 2k, 8h + 2k + 1
 
     template <int ST>
     __device__ __forceinline__ void stage(SoftmaxRow &sm) {
         if constexpr (ST == 0) {
-            e = fmaxf(s[0], s[1]);
-        } else if constexpr (ST < 8) {
-            e = fmaxf(e, fmaxf(s[2 * ST], s[2 * ST + 1]));
-        } else if constexpr (ST == 8) {
-            u = sm.update_from_max(row_max(e));
+            m0 = fmax3(s[0], s[1], s[2]);
+            m1 = fmax3(s[3], s[4], s[5]);
+            pin(m0), pin(m1);
+        } else if constexpr (ST == 1) {
+            m2 = fmax3(s[6], s[7], s[8]);
+            m3 = fmax3(s[9], s[10], s[11]);
+            pin(m2), pin(m3);
+        } else if constexpr (ST == 2) {
+            m4 = fmax3(s[12], s[13], s[14]);
+            m0 = fmax3(m0, m1, m2);
+            pin(m4), pin(m0);
+        } else if constexpr (ST == 3) {
+            m0 = fmaxf(fmax3(m0, m3, m4), s[15]);
+            pin(m0);
+        } else if constexpr (ST == 4) {
+            m0 = row_max(m0);
+            pin(m0);
+        } else if constexpr (ST == 5) {
+            // the reference moves when the block max passes it by more than kLazy (also for
+            // the first visible key); -inf stays -inf
+            const float m = m0 * sm.c;
+            mx = m > sm.m_ref + kLazy ? m : sm.m_ref;
+            pin(mx);
+        } else if constexpr (ST == 6) {
+            // alpha = 1 unless an existing reference moves; no branch
+            u.alpha = __builtin_amdgcn_exp2f((mx != sm.m_ref && sm.m_ref != -INFINITY) ? sm.m_ref - mx : 0.f);
+            sm.m_ref = mx;
+            u.m_use = mx == -INFINITY ? 0.f : mx;
             sum = 0.f;
+            pin(u.alpha), pin(u.m_use), pin(sm.m_ref), pin(sum);
         } else if constexpr (ST < kSmStages) {
-            constexpr int i = 2 * (ST - 9);
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], sm.c, -u.m_use));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], sm.c, -u.m_use));
-            sum += p0;
-            sum += p1;
-            const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
-            phi[i >> 3][i & 7] = h0;
-            phi[i >> 3][(i + 1) & 7] = h1;
-            plo[i >> 3][i & 7] = (__bf16)(p0 - (float)h0);
-            plo[i >> 3][(i + 1) & 7] = (__bf16)(p1 - (float)h1);
+            constexpr int k = (ST - kSmPre) / 4, r = (ST - kSmPre) % 4;
+            if constexpr (r == 0) {
+                const float x0 = __builtin_fmaf(s[2 * k], sm.c, -u.m_use);
+                x1 = __builtin_fmaf(s[2 * k + 1], sm.c, -u.m_use);
+                p0 = __builtin_amdgcn_exp2f(x0);
+                pin(x1), pin(p0);
+            } else if constexpr (r == 1) {
+                p1 = __builtin_amdgcn_exp2f(x1);
+                sum += p0;
+                pin(p1), pin(sum);
+            } else if constexpr (r == 2) {
+                sum += p1;
+                hp = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+                h0f = __uint_as_float(hp << 16);
+                pin(sum), pin(hp), pin(h0f);
+            } else {
+                const float l0 = p0 - h0f, l1 = p1 - __uint_as_float(hp & 0xffff0000u);
+                uint32_t lp = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){l0, l1}, bf16x2));
+                pin(lp);
+                phi[k >> 2][k & 3] = hp;
+                plo[k >> 2][k & 3] = lp;
+            }
         }
     }
 };
@@ -497,11 +559,14 @@ __device__ __forceinline__ f32x16 qk_block(const LDS_AS char *buf, const bf16x8 
 }
 
 // O^T += V^T P^T for 32 keys (block kb): for each 16-key step and 32-column tile, one V^T
-// fragment (two ds_read_b64_tr_b16) feeds the hi and the lo MFMA.  Fragments are read kPD
+// fragment (two ds_read_b64_tr_b16) feeds the hi and the lo MFMA.  Fragments are read PD
 // steps ahead; column tiles go in pairs so consecutive MFMAs use different accumulators.
+// fill(m) runs after MFMA m (0 .. 4*NT16-1): work issued there overlaps the matrix core.  P
+// is read at the MFMA that uses it, so fill may still be producing keys 16..31 (phi[1], plo[1])
+// during the first half of the chain.
 template <class Sh, int NT16, class F>
-__device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const bf16x8 (&phi)[2],
-                                         const bf16x8 (&plo)[2], f32x16 (&o)[NT16],
+__device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const u32x4 (&phi)[2],
+                                         const u32x4 (&plo)[2], f32x16 (&o)[NT16],
                                          const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1][2], F &&fill) {
     constexpr int NSTEP = 2 * NT16;     // (h16, t16) pairs
     constexpr int PD = 4;
@@ -519,14 +584,20 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const b
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, NSTEP / 2>([&](auto S2) {
         constexpr int st = 2 * decltype(S2)::value;
-        constexpr int h16 = st / NT16, t16 = st % NT16;
-        o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], phi[h16], o[t16], 0, 0, 0);
-        o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], phi[h16], o[t16 + 1], 0, 0, 0);
-        o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], plo[h16], o[t16], 0, 0, 0);
-        o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], plo[h16], o[t16 + 1], 0, 0, 0);
+        constexpr int h16 = st / NT16, t16 = st % NT16, m = 2 * st;
+        o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], __builtin_bit_cast(bf16x8, phi[h16]), o[t16], 0, 0, 0);
+        fill(IntC<m>{});
+        __builtin_amdgcn_sched_barrier(0);
+        o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], __builtin_bit_cast(bf16x8, phi[h16]), o[t16 + 1], 0, 0, 0);
+        fill(IntC<m + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], __builtin_bit_cast(bf16x8, plo[h16]), o[t16], 0, 0, 0);
         if constexpr (st + PD < NSTEP) vf[st % PD] = load(st + PD);
+        fill(IntC<m + 2>{});
+        __builtin_amdgcn_sched_barrier(0);
+        o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], __builtin_bit_cast(bf16x8, plo[h16]), o[t16 + 1], 0, 0, 0);
         if constexpr (st + 1 + PD < NSTEP) vf[(st + 1) % PD] = load(st + 1 + PD);
-        fill(S2);                                  // independent work for the MFMA shadow
+        fill(IntC<m + 3>{});
         __builtin_amdgcn_sched_barrier(0);
     });
 }
@@ -566,8 +637,8 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     const int64_t cache_row0 = a.offsets[b] + k0;
 
     using Dma = TileDma<Sh, T>;
-    auto dma_setup = [&](Dma &d, int t) {
-        LDS_AS char *buf = (LDS_AS char *)smem + (t & 1) * Sh::TILE_BYTES;
+    auto dma_setup = [&](Dma &d, int t, int bsel) {
+        LDS_AS char *buf = (LDS_AS char *)smem + bsel * Sh::TILE_BYTES;
         if (t < n_cache) {
             const int64_t left = k1 - k0 - (int64_t)t * kKeysPerTile;
             d.setup(buf, (const T *)a.ckv, a.ckv_stride, (const T *)a.krope, a.krope_stride,
@@ -583,7 +654,7 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     };
     {
         Dma d0;
-        dma_setup(d0, 0);
+        dma_setup(d0, 0, 0);
         d0.template issue<0, Dma::NINST>();
     }
 
@@ -665,55 +736,74 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             need_mask = true;
         }
         __builtin_amdgcn_sched_barrier(0);
-        // tile t+1 goes into the other buffer, its loads spread over this tile's MFMA chains
+        // tile t+1 goes into the other buffer
         const bool more = t + 1 < n_tiles;
         Dma dn;
-        if (more) dma_setup(dn, t + 1);
-        constexpr int P1 = Dma::NINST / 4, P2 = Dma::NINST / 2, P3 = 3 * Dma::NINST / 4;
-        if constexpr (!Sh::BF16)
-            if (more) dn.template issue<0, P1>();
 
         if constexpr (Sh::BF16) {
-            // Two 32-key halves.  Block 0: QK, then its softmax stages are interleaved with
-            // block 1's QK chain.  Block 1's softmax follows block 0's P.V chain.  The copy of
-            // tile t+1 is spread over the four chains; work a chain is too short to hold is done
-            // right after it (Spread::tail).
-            constexpr int NPV = NT16;                       // P.V steps per block (4 MFMAs each)
+            // Two 32-key blocks; every step of the softmax is placed between two MFMAs (see
+            // BlockSm).  The first half of a block's softmax (maxima, reference update, keys
+            // 0..15) must be done before its P.V chain starts; the second half (keys 16..31)
+            // only before the chain's MFMA 2*NT16, so it runs in the first slots of that chain.
+            //   QK0                                   (LDS-bound: nothing else)
+            //   QK1: block 0, first half
+            //   P.V0: block 0 second half | block 1 first half | copy set-up | copies 0..NINST/2
+            //   P.V1: block 1 second half | copies NINST/2..NINST
+            // The copy of tile t+1 goes into P.V chains (which leave LDS bandwidth to spare for
+            // the copied data to land), at most one per two MFMAs: faster, the copies outrun
+            // what one CU can fetch and stall the wave that issues them.  They are issued on
+            // every tile so that the chains have no branch: after the last tile they copy that
+            // tile again into the idle buffer, and the kernel waits for them before it exits.
+            constexpr int NPVM = 4 * NT16;                  // MFMAs per P.V chain
+            constexpr int H1 = kSmPre + 16;                 // steps of a softmax first half
+            constexpr int NC = Dma::NINST;
             BlockSm b0, b1;
-            using D0 = Spread<0, P1, 4, 1>;                 // loads [0, P1) at QK0 steps 4, 5, ...
-            b0.s = qk_block<Sh, NQ, 0>(buf, q, qk_base, [&](auto K) {
-                if (more) D0::template at<decltype(K)::value, NQ>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
-            });
-            if (more) D0::template tail<NQ>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            b0.s = qk_block<Sh, NQ, 0>(buf, q, qk_base, NoFill{});
             if (need_mask) mask_scores(b0.s, w0);
-            using S0 = Spread<0, kSmStages, 0, 2>;          // softmax of block 0 at QK1 steps 0, 2, 4, ...
-            using D1 = Spread<P1, P2, 1, 2>;                // loads [P1, P2) at QK1 steps 1, 3, ...
+            using A0 = Spread<0, H1, 0, 1>;
             b1.s = qk_block<Sh, NQ, 1>(buf, q, qk_base, [&](auto K) {
-                constexpr int k = decltype(K)::value;
-                S0::template at<k, NQ>([&](auto J) { b0.template stage<J.value>(sm); });
-                if (more) D1::template at<k, NQ>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+                A0::template at<decltype(K)::value, NQ>([&](auto J) { b0.template stage<J.value>(sm); });
             });
-            S0::template tail<NQ>([&](auto J) { b0.template stage<J.value>(sm); });
-            if (more) D1::template tail<NQ>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            A0::template tail<NQ>([&](auto J) { b0.template stage<J.value>(sm); });
             if (need_mask) mask_scores(b1.s, w1);
             if (__ballot(b0.u.alpha != 1.f)) rescale_acc<NT16>(o, b0.u.alpha);
-            // Block 1's softmax runs after block 0's P.V chain rather than inside it: placed
-            // inside, its VALU work lengthened the chain more than it saved.
-            using D2 = Spread<P2, P3, 0, 1>;
+            // The second half goes into the chain only if it is done by MFMA 2*NT16 (short
+            // chains, small d_c: it runs before the chain instead).
+            constexpr bool kIn = kSmStages - H1 <= 2 * NT16;
+            constexpr int H1e = kIn ? kSmStages : H1;
+            if constexpr (!kIn) static_for<H1, kSmStages>([&](auto J) { b0.template stage<J.value>(sm); });
+            using B0 = Spread<H1, H1e, 0, 1>;
+            using A1 = Spread<0, H1, kSmStages - H1, 1>;
+            constexpr int kSetup = kSmStages;
+            using C0 = Spread<0, NC / 2, kSetup + 1, 2>;
             pv_block<Sh, NT16>(buf, 0, b0.phi, b0.plo, o, pv_base, [&](auto K) {
-                if (more) D2::template at<decltype(K)::value, NPV>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+                constexpr int k = decltype(K)::value;
+                B0::template at<k, NPVM>([&](auto J) { b0.template stage<J.value>(sm); });
+                A1::template at<k, NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
+                if constexpr (k == kSetup) dma_setup(dn, more ? t + 1 : t, (t + 1) & 1);
+                C0::template at<k, NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
             });
-            if (more) D2::template tail<NPV>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
-            static_for<0, kSmStages>([&](auto J) { b1.template stage<J.value>(sm); });
-            sm.l = (sm.l * b0.u.alpha + b0.sum) * b1.u.alpha + b1.sum;
+            B0::template tail<NPVM>([&](auto J) { b0.template stage<J.value>(sm); });
+            A1::template tail<NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
+            if constexpr (kSetup >= NPVM) dma_setup(dn, more ? t + 1 : t, (t + 1) & 1);
+            C0::template tail<NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
             if (__ballot(b1.u.alpha != 1.f)) rescale_acc<NT16>(o, b1.u.alpha);
-            using D3 = Spread<P3, Dma::NINST, 0, 1>;
+            if constexpr (!kIn) static_for<H1, kSmStages>([&](auto J) { b1.template stage<J.value>(sm); });
+            using B1 = Spread<H1, H1e, 0, 1>;
+            using C1 = Spread<NC / 2, NC, kSmStages - H1, 2>;
             pv_block<Sh, NT16>(buf, 1, b1.phi, b1.plo, o, pv_base, [&](auto K) {
-                if (more) D3::template at<decltype(K)::value, NPV>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+                constexpr int k = decltype(K)::value;
+                B1::template at<k, NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
+                C1::template at<k, NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
             });
-            if (more) D3::template tail<NPV>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            B1::template tail<NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
+            C1::template tail<NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+            sm.l = (sm.l * b0.u.alpha + b0.sum) * b1.u.alpha + b1.sum;
         } else {
-            if (more) dn.template issue<P1, Dma::NINST>();
+            if (more) {
+                dma_setup(dn, t + 1, (t + 1) & 1);
+                dn.template issue<0, Dma::NINST>();
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
                 f32x16 sc = (f32x16){};
@@ -743,6 +833,7 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             }
         }
     }
+    wait_vm_all();                       // no copy may still be landing when the workgroup exits
     const float m_run = sm.m_ref, l_run = sm.l;
 
     // ---- epilogue: lane holds O^T[dc = t16*32 + (i/4)*8 + 4*half + i%4][row]
