@@ -8,8 +8,10 @@ split combine.  The default workload is the Kimi/DeepSeekV3-shape request (H = 6
 latent 512 + rope 64, bf16, committed cache 4096 tokens, a 64-node best-first draft tree).
 
 One JSON line is printed.  `value` is algorithmic TFLOP/s of the whole step;
-`roofline` rates the attention kernel alone (HIP events on the stream it runs on) against
-the bf16 MFMA peak; `cpu_baseline` times the fp64 oracle on the host cores.
+`roofline` rates the attention kernel alone (HIP events around each of its launches in the
+timed region, on the stream it runs on) against the bf16 MFMA peak, with `traffic` the HBM
+bytes per launch from the committed rocprofv3 counter summary (null when the kernel sources
+changed since it was taken); `cpu_baseline` times the fp64 oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -94,28 +96,29 @@ def run(args):
     if int(status.item()) != 0:
         raise SystemExit(f"device status {int(status.item())} on the benchmark inputs")
 
-    # ---- timed region: K whole steps
+    # ---- timed region: K whole steps; the attention kernel's own launches are bracketed by
+    # events on the stream it runs on (the same stream as the rest of the step)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def timed_step(i):
+        kdt.build_visibility(parents, out=masks, dev_status=status, stream=stream)
+        kdt.plan(lens, desc, ws, dev_status=status, stream=stream)
+        evs[i][0].record(stream)
+        kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
+        evs[i][1].record(stream)
+        kdt.combine(out, desc, ws, stream=stream)
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        timed_step(i)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     step_ms = ev0.elapsed_time(ev1) / args.steps
-
-    # ---- the attention kernel alone, each launch bracketed by events on its stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in evs:
-        a.record(stream)
-        kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
-        b.record(stream)
-    torch.cuda.synchronize()
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    kdt.combine(out, desc, ws, stream=stream)
-    torch.cuda.synchronize()
 
     peak = PEAK_BF16_TFLOPS if sp.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops / (attn_ms * 1e-3) / 1e12
@@ -143,6 +146,7 @@ def run(args):
         "alg_gflop_per_step": round(flops / 1e9, 4),
         "alg_mbytes_per_step": round(nbytes / 1e6, 4),
         "attn_kernel_ms": round(attn_ms, 5),
+        "kernel_source_hash": kernel_source_hash(),
         "wall_ms_timed_region": round(wall_ms, 3),
         "roofline": {
             "bound": "mfma",
@@ -150,24 +154,63 @@ def run(args):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(sp.name),
         },
     }
     return line, inp
 
 
-def cpu_baseline(inp):
-    """The fp64 oracle on the host cores: masks + every output row of one step."""
+def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0):
+    """The fp64 oracle on the host cores: whole steps (masks + every output row) of the same
+    workload, repeated until about min_seconds of CPU work (at most max_seconds)."""
     import oracle
     cores = len(os.sched_getaffinity(0))
     flops, _, _ = algorithmic_work(inp)
     oracle.build()
-    t0 = time.perf_counter()
-    oracle.run(inp, threads=cores)
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"one whole step of the same workload (masks + all {inp.spec.batch * inp.spec.nodes * inp.spec.heads}"
-                      f" rows, fp64), {dt:.2f} s"}
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run(inp, threads=cores)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or dt * (reps + 1) / reps > max_seconds:
+            break
+    rows = inp.spec.batch * inp.spec.nodes * inp.spec.heads
+    return {"value": round(reps * flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} whole step(s) of the same workload (masks + all {rows} rows, fp64) "
+                      f"in {dt:.2f} s on {cores} threads"}
+
+
+# HBM traffic of the attention kernel per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# summarised under profiles/.  The summary records a hash of the kernel sources it was taken
+# on; when the sources have changed since, the figure no longer describes this kernel and
+# `traffic` is reported as null.
+def kernel_source_hash() -> str:
+    import hashlib
+    import glob
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_verify_mla_02_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    path = os.path.join(ROOT, "profiles", f"verify_attn_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
