@@ -137,7 +137,7 @@ kdt::AttnArgs make_args(const kdt_verify_desc &d, const kdt::Geometry &g, void *
     a.hdr = (const kdt::WsHeader *)(w + g.off_header);
     a.offsets = (const int64_t *)(w + g.off_offsets);
     a.lens = (const int32_t *)(w + g.off_lens);
-    a.units = (const int4 *)(w + g.off_units);
+    a.units = (const kdt::Unit *)(w + g.off_units);
     a.part_ml = g.off_ml ? (float2 *)(w + g.off_ml) : nullptr;
     a.part_o = g.off_o ? (float *)(w + g.off_o) : nullptr;
     return a;
@@ -174,6 +174,7 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     x.nsplit = (int)S;
     x.chunk = chunk;
     // one group of RT units per (request, split); groups are dealt to 8 XCD lanes of the grid
+    // (the row tiles of a split share its keys through one L2)
     const int64_t groups = (int64_t)d.batch * S;
     x.units = (groups + 7) / 8 * 8 * rt;
     if (x.units > INT32_MAX) return false;
@@ -189,7 +190,7 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     x.off_lens = take(4 * B);
     x.off_gwork = take(8 * (size_t)groups);
     x.off_gorder = take(4 * (size_t)groups);
-    x.off_units = take(16 * (size_t)x.units);
+    x.off_units = take(sizeof(kdt::Unit) * (size_t)x.units);
     if (S > 1) {
         x.off_ml = take(8 * (size_t)B * S * x.rows);
         x.off_o = take(4 * (size_t)B * S * x.rows * d.d_latent);

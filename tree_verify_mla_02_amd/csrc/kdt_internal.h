@@ -41,6 +41,16 @@ struct WsHeader {
     int32_t pad[63];
 };
 
+// One workgroup's share of the attention, written by the plan: everything the kernel needs
+// to start, in one 32-byte scalar load.  b < 0 marks an empty grid slot (also every slot
+// when the plan rejected cache_lens).
+struct Unit {
+    int32_t b, rt, s, sb;      // request, row tile, split, splits of that request
+    int32_t k0, k1;            // cache keys [k0, k1) of this split, request-relative
+    int64_t row0;              // packed-cache row of key k0
+};
+static_assert(sizeof(Unit) == 32, "one 32-byte record");
+
 struct AttnArgs {
     const void *q_lat, *q_rope, *ckv, *krope, *tckv, *tkrope;
     const uint64_t *masks;
@@ -54,7 +64,7 @@ struct AttnArgs {
     const WsHeader *hdr;
     const int64_t *offsets;
     const int32_t *lens;
-    const int4 *units;     // (b, rt, s, splits of b); b < 0 marks an empty slot
+    const Unit *units;     // one per grid slot
     float2 *part_ml;       // [B][S][R] (running max in log2 domain, sum)
     float *part_o;         // [B][S][R][d_c] un-normalised partial outputs
 };

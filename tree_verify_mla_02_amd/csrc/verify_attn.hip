@@ -77,7 +77,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
                                                     int64_t max_len, int64_t total_len, int RT, int S,
                                                     int64_t chunk, int64_t U, WsHeader *hdr,
                                                     int64_t *offsets, int32_t *lens, int64_t *gwork,
-                                                    int32_t *gorder, int4 *units, int32_t *dev_status) {
+                                                    int32_t *gorder, Unit *units, int32_t *dev_status) {
     __shared__ int s_ok;
     const int tid = threadIdx.x, nth = blockDim.x;
     if (tid == 0) s_ok = 1;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
         }
         gwork[g] = w;
     }
-    for (int64_t u = tid; u < U; u += nth) units[u] = make_int4(-1, 0, 0, 0);
+    for (int64_t u = tid; u < U; u += nth) units[u] = Unit{-1, 0, 0, 0, 0, 0, 0};
     __syncthreads();
     for (int64_t g = tid; g < G; g += nth) {
         int64_t rank = g;
@@ -127,6 +127,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
         gorder[rank] = (int32_t)g;
     }
     __syncthreads();
+    // Group p (in work order) goes to XCD lane x in snake order over rounds of 8 groups; its
+    // row tile rt takes grid slot x + 8 * (round * RT + rt).  Slots are dealt to the XCDs
+    // round-robin, so a group runs on one XCD.
     for (int64_t e = tid; e < G * RT; e += nth) {
         const int64_t p = e / RT;
         const int rt = (int)(e % RT);
@@ -136,7 +139,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
         const int j = (int)(p % kXcds);
         const int x = (round & 1) ? kXcds - 1 - j : j;
         const int b = g / S, sp = g % S;
-        units[x + kXcds * (round * RT + rt)] = make_int4(b, rt, sp, splits_of(lens[b], chunk, S));
+        const int64_t k0 = (int64_t)sp * chunk;
+        const int64_t k1 = k0 + chunk < (int64_t)lens[b] ? k0 + chunk : (int64_t)lens[b];
+        units[x + kXcds * (round * RT + rt)] =
+            Unit{b, rt, sp, splits_of(lens[b], chunk, S), (int32_t)k0, (int32_t)k1, offsets[b] + k0};
     }
 }
 
@@ -610,10 +616,11 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     constexpr int NQ = Sh::BF16 ? D / 16 : D / 2;       // query fragments per lane
     __shared__ __attribute__((aligned(1024))) char smem[2 * Sh::TILE_BYTES];
 
-    if (!a.hdr->ok) return;
-    const int4 unit = a.units[blockIdx.x];
-    if (unit.x < 0) return;
-    const int b = unit.x, rt = unit.y, s = unit.z, sb = unit.w;
+    // One scalar load: a slot the plan left empty (or every slot, when it rejected the
+    // cache lengths) has b < 0.
+    const Unit unit = a.units[blockIdx.x];
+    if (unit.b < 0) return;
+    const int b = unit.b, rt = unit.rt, s = unit.s, sb = unit.sb;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps LDS bases in SGPRs
     const int half = lane >> 5;                          // 0: lanes 0-31, 1: lanes 32-63
@@ -628,13 +635,11 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     const T *qrope = (const T *)a.q_rope + ((int64_t)b * R + rc) * a.q_rope_stride;
 
     // ---- key ranges: cache keys [k0, k1) of this split, then the tree keys if s == 0
-    const int L = a.lens[b];
-    const int64_t k0 = (int64_t)s * a.chunk;
-    const int64_t k1 = (k0 + a.chunk < (int64_t)L) ? k0 + a.chunk : (int64_t)L;
+    const int64_t k0 = unit.k0, k1 = unit.k1;
     const int n_cache = k1 > k0 ? (int)(((k1 - k0) + kKeysPerTile - 1) / kKeysPerTile) : 0;
     const int n_tree = (s == 0) ? (a.N + kKeysPerTile - 1) / kKeysPerTile : 0;
     const int n_tiles = n_cache + n_tree;
-    const int64_t cache_row0 = a.offsets[b] + k0;
+    const int64_t cache_row0 = unit.row0;
 
     using Dma = TileDma<Sh, T>;
     auto dma_setup = [&](Dma &d, int t, int bsel) {
@@ -658,15 +663,52 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
         d0.template issue<0, Dma::NINST>();
     }
 
+    // per-lane LDS byte offsets (see lds_off) of the few swizzle patterns this lane reads
+    constexpr int QK_PAT = Sh::CB / 2;                       // K reads: chunk 2kk + half
+    constexpr int PV_PAT = Sh::CB >= 8 ? Sh::CB / 4 : 1;     // V^T reads: chunk 4*t16 + y
+    int qk_base[QK_PAT], pv_base[PV_PAT][2];
+#pragma unroll
+    for (int j = 0; j < QK_PAT; j++) qk_base[j] = lds_off<Sh>(lane & 31, 2 * j + half);
+    {
+        const int w = 4 * half + ((lane & 15) >> 2);              // key within an 8-key group
+        const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within 4 chunks (32 columns)
+#pragma unroll
+        for (int j = 0; j < PV_PAT; j++)
+#pragma unroll
+            for (int e = 0; e < 2; e++) pv_base[j][e] = lds_off<Sh>(w + 8 * e, 4 * j + y) + 8 * (lane & 1);
+    }
+
     // ---- queries to registers: B operand of S^T = K Q^T
     typedef typename std::conditional<Sh::BF16, bf16x8, float>::type QFrag;
     QFrag q[NQ];
     if constexpr (Sh::BF16) {
+        // The workgroup's 128 query rows go through LDS: each half (64 rows) is copied into
+        // buffer 1 exactly like a key tile (full 128-byte row segments per copy, swizzled 1 KB
+        // blocks) while tile 0 lands in buffer 0, and the two waves owning those rows read
+        // their fragments with the K-fragment pattern.  Loading the fragments straight from
+        // HBM touches 32 rows x 32 bytes per instruction, a quarter of each fetched line.
+        LDS_AS char *qbuf = (LDS_AS char *)smem + Sh::TILE_BYTES;
 #pragma unroll
-        for (int kk = 0; kk < NQ; kk++) {
-            const int d0 = 16 * kk + 8 * half;
-            const T *src = (16 * kk < DC) ? qlat + d0 : qrope + (d0 - DC);
-            q[kk] = *(const bf16x8 *)src;
+        for (int h = 0; h < 2; h++) {
+            int64_t first = (int64_t)rt * kRowsPerTile + 64 * h;
+            int64_t nrows = R - first;
+            if (nrows <= 0) {                  // no row of this half exists: copy a valid one
+                first = R - 1;
+                nrows = 1;
+            }
+            Dma dq;
+            dq.setup(qbuf, (const T *)a.q_lat, a.q_lat_stride, (const T *)a.q_rope, a.q_rope_stride,
+                     (int64_t)b * R + first, nrows < 64 ? (int)nrows : 64, wave, lane);
+            if (h == 1) __syncthreads();       // waves 0 and 1 are done reading half 0
+            dq.template issue<0, Dma::NINST>();
+            wait_vm_all();
+            __syncthreads();
+            if (wave / 2 == h) {
+                const LDS_AS char *src = qbuf + key_off<Sh>(32 * (wave % 2));
+#pragma unroll
+                for (int kk = 0; kk < NQ; kk++)
+                    q[kk] = *(const LDS_AS bf16x8 *)(src + qk_base[kk % QK_PAT] + (kk / QK_PAT) * 1024);
+            }
         }
     } else {
 #pragma unroll
@@ -685,21 +727,6 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int kk = 0; kk < NQ; kk++) q[kk] = zero ? q[kk] * (T)0.f : -q[kk];
         c_pos = zero ? 1.f : -c_pos;
-    }
-
-    // per-lane LDS byte offsets (see lds_off) of the few swizzle patterns this lane reads
-    constexpr int QK_PAT = Sh::CB / 2;                       // K reads: chunk 2kk + half
-    constexpr int PV_PAT = Sh::CB >= 8 ? Sh::CB / 4 : 1;     // V^T reads: chunk 4*t16 + y
-    int qk_base[QK_PAT], pv_base[PV_PAT][2];
-#pragma unroll
-    for (int j = 0; j < QK_PAT; j++) qk_base[j] = lds_off<Sh>(lane & 31, 2 * j + half);
-    {
-        const int w = 4 * half + ((lane & 15) >> 2);              // key within an 8-key group
-        const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // chunk within 4 chunks (32 columns)
-#pragma unroll
-        for (int j = 0; j < PV_PAT; j++)
-#pragma unroll
-            for (int e = 0; e < 2; e++) pv_base[j][e] = lds_off<Sh>(w + 8 * e, 4 * j + y) + 8 * (lane & 1);
     }
 
     f32x16 o[NT16];
@@ -911,7 +938,7 @@ hipError_t launch_plan(const int32_t *cache_lens, const kdt_verify_desc &d, cons
                                     g.row_tiles, g.nsplit, g.chunk, g.units, (WsHeader *)(w + g.off_header),
                                     (int64_t *)(w + g.off_offsets), (int32_t *)(w + g.off_lens),
                                     (int64_t *)(w + g.off_gwork), (int32_t *)(w + g.off_gorder),
-                                    (int4 *)(w + g.off_units), dev_status);
+                                    (Unit *)(w + g.off_units), dev_status);
     return hipGetLastError();
 }
 
