@@ -1,6 +1,7 @@
 """Benchmark of the tree-verify MLA-absorb attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kimi] [--no-cpu-baseline]
+                    [--cold-steps C]
 
 A step is one pass of the whole path over one synthetic batch already resident in HBM:
 ancestor bitmasks from the parent array, the ragged plan, the attention kernel and the
@@ -9,7 +10,8 @@ latent 512 + rope 64, bf16, committed cache 4096 tokens, a 64-node best-first dr
 
 One JSON line is printed.  `value` is algorithmic TFLOP/s of the whole step;
 `roofline` rates the attention kernel alone (HIP events around each of its launches in the
-timed region, on the stream it runs on) against the bf16 MFMA peak, with `traffic` the HBM
+timed region, on the stream it runs on) against the roof that binds it (bf16 MFMA peak, or
+HBM bandwidth when the algorithmic intensity is below the ridge point), with `traffic` the HBM
 bytes per launch from the committed rocprofv3 counter summary (null when the kernel sources
 changed since it was taken); `cpu_baseline` times the fp64 oracle on the host cores.
 """
@@ -118,10 +120,37 @@ def run(args):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     step_ms = ev0.elapsed_time(ev1) / args.steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    attn_each = np.array([a.elapsed_time(b) for a, b in evs])
+    attn_ms = float(attn_each.mean())
 
-    peak = PEAK_BF16_TFLOPS if sp.dtype == "bf16" else PEAK_F32_TFLOPS
-    achieved = flops / (attn_ms * 1e-3) / 1e12
+    # ---- cold caches: before each of a few attention launches, write a 512 MiB scratch buffer
+    # (twice the 256 MB Infinity Cache) so the launch starts with cold L2 and MALL
+    cold = []
+    if args.cold_steps:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        for _ in range(args.cold_steps):
+            scratch.fill_(1)
+            kdt.build_visibility(parents, out=masks, dev_status=status, stream=stream)
+            kdt.plan(lens, desc, ws, dev_status=status, stream=stream)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
+            a1.record(stream)
+            kdt.combine(out, desc, ws, stream=stream)
+            torch.cuda.synchronize()
+            cold.append(a0.elapsed_time(a1))
+        del scratch
+
+    # the roof that binds: MFMA when the algorithmic intensity is above the ridge point
+    mfma_peak = PEAK_BF16_TFLOPS if sp.dtype == "bf16" else PEAK_F32_TFLOPS
+    ridge = mfma_peak * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    hbm_bound = flops / nbytes < ridge
+    if hbm_bound:
+        bound, peak, unit_r = "hbm", PEAK_HBM_GBPS, "GB/s"
+        achieved = nbytes / (attn_ms * 1e-3) / 1e9
+    else:
+        bound, peak, unit_r = "mfma", mfma_peak, "TFLOP/s"
+        achieved = flops / (attn_ms * 1e-3) / 1e12
     value = flops / (step_ms * 1e-3) / 1e12
     line = {
         "metric": "tree-verify attn TFLOP/s + cache GB/s, % of MI355X roofline, Kimi-shape N=64 tree",
@@ -146,13 +175,16 @@ def run(args):
         "alg_gflop_per_step": round(flops / 1e9, 4),
         "alg_mbytes_per_step": round(nbytes / 1e6, 4),
         "attn_kernel_ms": round(attn_ms, 5),
+        "attn_kernel_ms_p10_p50_p90": [round(float(np.percentile(attn_each, q)), 5) for q in (10, 50, 90)],
+        "attn_kernel_cold_ms_median": round(float(np.median(cold)), 5) if cold else None,
+        "arith_intensity_flop_per_byte": round(flops / nbytes, 1),
         "kernel_source_hash": kernel_source_hash(),
         "wall_ms_timed_region": round(wall_ms, 3),
         "roofline": {
-            "bound": "mfma",
+            "bound": bound,
             "achieved": round(achieved, 3),
             "peak": peak,
-            "unit": "TFLOP/s",
+            "unit": unit_r,
             "frac": round(achieved / peak, 4),
             "traffic": recorded_traffic(sp.name),
         },
@@ -221,6 +253,8 @@ def main():
     ap.add_argument("--workload", default="kimi", choices=sorted(workloads.SPECS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="attention launches timed after flushing L2 and MALL (0 to skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (to scale HBM byte counters)")
     args = ap.parse_args()
