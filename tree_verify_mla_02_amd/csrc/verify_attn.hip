@@ -890,44 +890,89 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     }
 }
 
+// Reductions over the 64 lanes of a wave (butterfly).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
 // ------------------------------------------------------------------------------ combine
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, for rows of split
 // requests.  One wave per row; lane handles 8 consecutive output columns.
 template <int DC>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
-    if (!a.hdr->ok) return;
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= (int64_t)a.B * a.R) return;
     const int b = (int)(row / a.R);
     const int64_t r = row - (int64_t)b * a.R;
+    const int ok = a.hdr->ok;                         // both loads in flight together
     const int sb = splits_of(a.lens[b], a.chunk, a.S);
-    if (sb <= 1) return;
+    if (!ok || sb <= 1) return;
     const int64_t prow0 = (int64_t)b * a.S * a.R + r;
+    // (max, sum) of split s sits in lane s % 64: the row max M and the denominator are wave
+    // reductions, and split s's weight 2^(m_s - M) is broadcast from its lane.
     float M = -INFINITY;
-    for (int s = 0; s < sb; s++) M = fmaxf(M, a.part_ml[prow0 + (int64_t)s * a.R].x);
-    constexpr int PER = 8;
-    if (lane * PER >= DC) return;
+    for (int s0 = 0; s0 < sb; s0 += 64)
+        if (s0 + lane < sb) M = fmaxf(M, a.part_ml[prow0 + (int64_t)(s0 + lane) * a.R].x);
+    M = wave_max(M);
+    constexpr int PER = DC / 64;                      // output columns per lane
+    static_assert(PER == 8 || PER == 1, "columns per lane");
     float acc[PER];
 #pragma unroll
     for (int k = 0; k < PER; k++) acc[k] = 0.f;
     float den = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < sb; s++) {
-            const int64_t prow = prow0 + (int64_t)s * a.R;
-            const float2 ml = a.part_ml[prow];
-            const float w = __builtin_amdgcn_exp2f(ml.x - M);
-            den += w * ml.y;
-            const float4 *src = (const float4 *)(a.part_o + prow * DC + lane * PER);
-            const float4 x0 = src[0], x1 = src[1];
-            acc[0] += w * x0.x; acc[1] += w * x0.y; acc[2] += w * x0.z; acc[3] += w * x0.w;
-            acc[4] += w * x1.x; acc[5] += w * x1.y; acc[6] += w * x1.z; acc[7] += w * x1.w;
+        for (int s0 = 0; s0 < sb; s0 += 64) {
+            float w = 0.f;
+            if (s0 + lane < sb) {
+                const float2 ml = a.part_ml[prow0 + (int64_t)(s0 + lane) * a.R];
+                w = __builtin_amdgcn_exp2f(ml.x - M);
+                den += w * ml.y;
+            }
+            const int n = sb - s0 < 64 ? sb - s0 : 64;
+            constexpr int U = 4;                      // splits whose rows are in flight together
+            for (int s = 0; s < n; s += U) {
+                float xs[U][PER];
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    if (s + u < n) {
+                        const float *src = a.part_o + (prow0 + (int64_t)(s0 + s + u) * a.R) * DC + lane * PER;
+                        if constexpr (PER == 8) {
+                            const float4 x0 = ((const float4 *)src)[0], x1 = ((const float4 *)src)[1];
+                            xs[u][0] = x0.x; xs[u][1] = x0.y; xs[u][2] = x0.z; xs[u][3] = x0.w;
+                            xs[u][4] = x1.x; xs[u][5] = x1.y; xs[u][6] = x1.z; xs[u][7] = x1.w;
+                        } else {
+                            xs[u][0] = src[0];
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    if (s + u < n) {
+                        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
+#pragma unroll
+                        for (int k = 0; k < PER; k++) acc[k] += ws * xs[u][k];
+                    }
+                }
+            }
         }
+        den = wave_sum(den);
     }
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    float4 *dst = (float4 *)(a.out + row * DC + lane * PER);
-    dst[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-    dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    float *dst = a.out + row * DC + lane * PER;
+    if constexpr (PER == 8) {
+        ((float4 *)dst)[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        ((float4 *)dst)[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    } else {
+        dst[0] = acc[0] * inv;
+    }
 }
 
 // ------------------------------------------------------------------------------ launchers
