@@ -4,8 +4,8 @@
                     [--cold-steps C]
 
 A step is one pass of the whole path over one synthetic batch already resident in HBM:
-ancestor bitmasks from the parent array, the ragged plan, the attention kernel and the
-split combine.  The default workload is the Kimi/DeepSeekV3-shape request (H = 64 heads,
+ancestor bitmasks from the parent array and the ragged plan (one fused launch), the attention
+kernel and the split combine.  The default workload is the Kimi/DeepSeekV3-shape request (H = 64 heads,
 latent 512 + rope 64, bf16, committed cache 4096 tokens, a 64-node best-first draft tree).
 
 One JSON line is printed.  `value` is algorithmic TFLOP/s of the whole step;
@@ -87,8 +87,7 @@ def run(args):
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        kdt.build_visibility(parents, out=masks, dev_status=status, stream=stream)
-        kdt.plan(lens, desc, ws, dev_status=status, stream=stream)
+        kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
         kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
         kdt.combine(out, desc, ws, stream=stream)
 
@@ -103,8 +102,7 @@ def run(args):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
 
     def timed_step(i):
-        kdt.build_visibility(parents, out=masks, dev_status=status, stream=stream)
-        kdt.plan(lens, desc, ws, dev_status=status, stream=stream)
+        kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
         evs[i][0].record(stream)
         kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
         evs[i][1].record(stream)
@@ -130,8 +128,7 @@ def run(args):
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         for _ in range(args.cold_steps):
             scratch.fill_(1)
-            kdt.build_visibility(parents, out=masks, dev_status=status, stream=stream)
-            kdt.plan(lens, desc, ws, dev_status=status, stream=stream)
+            kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record(stream)
             kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)

@@ -151,6 +151,19 @@ int kdt_tree_verify_attend(const void *q_lat, const void *q_rope, const void *ck
 int kdt_tree_verify_combine(float *out, const kdt_verify_desc *desc, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/*
+ * kdt_tree_verify_prepare -- kdt_build_visibility and kdt_tree_verify_plan in one launch
+ * (the two are independent; a verify step needs both before the attention).
+ *   parents   [B, N] int32, device, with B = desc->batch and N = desc->num_nodes; bitmask
+ *             [B, N, ceil(N/64)] uint64 -- exactly as kdt_build_visibility.
+ *   cache_lens, workspace, dev_status -- exactly as kdt_tree_verify_plan.
+ * Host-side errors are those of the two calls; device-side errors OR the same bits into
+ * *dev_status.
+ */
+int kdt_tree_verify_prepare(const int32_t *parents, uint64_t *bitmask, const int32_t *cache_lens,
+                            const kdt_verify_desc *desc, void *workspace, size_t workspace_bytes,
+                            int32_t *dev_status, void *stream);
+
 /* Number of key splits per request the plan uses for desc on the current device (1 = no
  * split), or -1 for an invalid desc. */
 int kdt_tree_verify_num_splits(const kdt_verify_desc *desc);

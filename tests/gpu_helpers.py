@@ -49,13 +49,27 @@ def to_device(inp: workloads.Inputs) -> DevInputs:
                      q_rope=inp.q_rope.cuda(), kv=kv.cuda(), tree_kv=inp.tree_kv.cuda(), dc=inp.spec.d_latent)
 
 
-def run_gpu(inp: workloads.Inputs, dev: DevInputs = None, staged: bool = False):
-    """Masks [B,N,W] (numpy uint64) and outputs [B,N,H,d_c] (torch fp32, on device)."""
+def run_gpu(inp: workloads.Inputs, dev: DevInputs = None, staged=False):
+    """Masks [B,N,W] (numpy uint64) and outputs [B,N,H,d_c] (torch fp32, on device).
+
+    staged: False = kdt_build_visibility + kdt_tree_verify_attn; True = visibility, plan,
+    attend, combine as separate calls; "prepare" = kdt_tree_verify_prepare (masks and plan
+    in one launch), attend, combine."""
     dev = dev or to_device(inp)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
-    masks = kdt.build_visibility(dev.parents, dev_status=status)
     maxL = int(inp.cache_lens.max()) if inp.cache_lens.numel() else 0
     total = inp.total_len
+    if staged == "prepare":
+        desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, maxL, total)
+        ws = kdt.alloc_workspace(desc)
+        out = torch.empty(dev.q_lat.shape, dtype=torch.float32, device="cuda")
+        masks = kdt.prepare(dev.parents, dev.cache_lens, desc, ws, dev_status=status)
+        kdt.attend(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, masks, inp.scale, out,
+                   desc, ws)
+        kdt.combine(out, desc, ws)
+        torch.cuda.synchronize()
+        return masks.cpu().numpy().view(np.uint64), out, int(status.item())
+    masks = kdt.build_visibility(dev.parents, dev_status=status)
     if not staged:
         out = kdt.tree_verify_attn(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, masks,
                                    dev.cache_lens, inp.scale, dev_status=status, max_cache_len=maxL,

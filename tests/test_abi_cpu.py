@@ -50,6 +50,25 @@ def test_visibility_rejects_bad_arguments_on_host():
     assert lib.kdt_build_visibility(ctypes.c_void_p((1 << 20) + 2), 1, 4, fake, None, None) == _lib.KDT_ERR_MISALIGNED
 
 
+def test_prepare_rejects_bad_arguments_on_host():
+    lib = kdt.load()
+    d = _lib.VerifyDesc(batch=1, num_nodes=8, num_heads=4, d_latent=512, d_rope=64, dtype=_lib.KDT_BF16,
+                        max_cache_len=16, total_cache_len=16, q_lat_stride=512, q_rope_stride=64, ckv_stride=576,
+                        krope_stride=576, tree_ckv_stride=576, tree_krope_stride=576)
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: every call fails before any launch
+    assert lib.kdt_tree_verify_prepare(None, fake, fake, ctypes.byref(d), fake, 1 << 20, None, None) == \
+        _lib.KDT_ERR_INVALID_ARG
+    assert lib.kdt_tree_verify_prepare(fake, fake, None, ctypes.byref(d), fake, 1 << 20, None, None) == \
+        _lib.KDT_ERR_INVALID_ARG
+    assert lib.kdt_tree_verify_prepare(ctypes.c_void_p((1 << 20) + 2), fake, fake, ctypes.byref(d), fake, 1 << 20,
+                                       None, None) == _lib.KDT_ERR_MISALIGNED
+    assert lib.kdt_tree_verify_prepare(fake, ctypes.c_void_p((1 << 20) + 4), fake, ctypes.byref(d), fake, 1 << 20,
+                                       None, None) == _lib.KDT_ERR_MISALIGNED
+    d.num_nodes = 300
+    assert lib.kdt_tree_verify_prepare(fake, fake, fake, ctypes.byref(d), fake, 1 << 20, None, None) == \
+        _lib.KDT_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("num_nodes", 0, _lib.KDT_ERR_UNSUPPORTED), ("num_nodes", 300, _lib.KDT_ERR_UNSUPPORTED),
     ("batch", 0, _lib.KDT_ERR_INVALID_ARG), ("num_heads", 0, _lib.KDT_ERR_INVALID_ARG),

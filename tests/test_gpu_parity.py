@@ -104,6 +104,35 @@ def test_chain_equals_causal_prefill_on_gpu():
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("name", ["tiny", "kimi", "block8", "wide"])
+def test_prepare_equals_separate_calls(name):
+    """kdt_tree_verify_prepare (masks + plan in one launch) gives the same masks, status and
+    outputs, bit for bit, as kdt_build_visibility + kdt_tree_verify_plan; and passes parity."""
+    inp = workloads.make_inputs(name, seed=3)
+    if name == "wide":
+        inp = workloads.subset_requests(inp, [0, 5])
+    dev = to_device(inp)
+    m1, o1, s1 = run_gpu(inp, dev=dev, staged=True)
+    m2, o2, s2 = run_gpu(inp, dev=dev, staged="prepare")
+    np.testing.assert_array_equal(m1, m2)
+    assert s1 == s2
+    assert torch.equal(o1, o2)
+    rows = None if name in ("tiny", "block8") else sample_rows(inp, per_request=8)
+    check(f"{name}-prepare", inp, rows=rows, staged="prepare", dev=dev)
+
+
+def test_prepare_flags_bad_parents_and_lengths():
+    spec = workloads.Spec("prepbad", 53, 2, 8, 4, 512, 64, "bf16", 100, tree="random")
+    par = workloads.make_parents(spec, 0)
+    par[1, 4] = 4          # its own parent
+    inp = workloads.make_inputs(spec, seed=0, parents=par)
+    masks, _, status = run_gpu(inp, staged="prepare")
+    assert status & kdt._lib.KDT_DEV_BAD_PARENT
+    ref_masks, bad = oracle.visibility(inp.parents.numpy())
+    assert bad > 0
+    np.testing.assert_array_equal(masks, ref_masks)
+
+
 # ------------------------------------------------------------------ edge cases and properties
 def test_invalid_parents_flag_and_zero_rows():
     spec = workloads.Spec("badpar", 51, 2, 8, 4, 512, 64, "bf16", 100, tree="random")

@@ -5,7 +5,7 @@ this package is its Python binding.  Build the library with
 ``python -m tree_verify_mla_02_amd.build``.
 """
 from ._lib import (KdtError, VerifyDesc, alloc_workspace, attend, build_visibility, combine, load,
-                   make_desc, num_splits, plan, tree_verify_attn, workspace_size)
+                   make_desc, num_splits, plan, prepare, tree_verify_attn, workspace_size)
 
 __all__ = ["KdtError", "VerifyDesc", "alloc_workspace", "attend", "build_visibility", "combine", "load",
-           "make_desc", "num_splits", "plan", "tree_verify_attn", "workspace_size"]
+           "make_desc", "num_splits", "plan", "prepare", "tree_verify_attn", "workspace_size"]

@@ -21,7 +21,7 @@ KDT_BF16, KDT_F32 = 0, 1
 
 EXPORTS = [
     "kdt_build_visibility", "kdt_tree_verify_workspace_size", "kdt_tree_verify_attn",
-    "kdt_tree_verify_plan", "kdt_tree_verify_attend", "kdt_tree_verify_combine",
+    "kdt_tree_verify_plan", "kdt_tree_verify_prepare", "kdt_tree_verify_attend", "kdt_tree_verify_combine",
     "kdt_tree_verify_num_splits", "kdt_status_string", "kdt_last_error", "kdt_last_status", "kdt_version",
 ]
 
@@ -62,6 +62,7 @@ def load() -> ctypes.CDLL:
     lib.kdt_tree_verify_num_splits.argtypes = [dp]
     lib.kdt_tree_verify_attn.argtypes = [vp] * 8 + [ctypes.c_float, vp, dp, vp, sz, vp, vp]
     lib.kdt_tree_verify_plan.argtypes = [vp, dp, vp, sz, vp, vp]
+    lib.kdt_tree_verify_prepare.argtypes = [vp, vp, vp, dp, vp, sz, vp, vp]
     lib.kdt_tree_verify_attend.argtypes = [vp] * 7 + [ctypes.c_float, vp, dp, vp, sz, vp]
     lib.kdt_tree_verify_combine.argtypes = [vp, dp, vp, sz, vp]
     lib.kdt_status_string.restype = ctypes.c_char_p
@@ -195,6 +196,19 @@ def tree_verify_attn(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, bitmask, c
 def plan(cache_lens, desc: VerifyDesc, workspace, dev_status=None, stream=None):
     _check(load().kdt_tree_verify_plan(_ptr(cache_lens), ctypes.byref(desc), _ptr(workspace), workspace.numel(),
                                        _ptr(dev_status), _stream(stream)))
+
+
+def prepare(parents, cache_lens, desc: VerifyDesc, workspace, masks_out: Optional[torch.Tensor] = None,
+            dev_status=None, stream=None) -> torch.Tensor:
+    """Masks [B, N, ceil(N/64)] (int64 view of uint64) and the plan in `workspace`, one launch."""
+    if parents.dtype != torch.int32 or not parents.is_contiguous() or parents.dim() != 2:
+        raise ValueError("parents must be a contiguous [B, N] int32 tensor")
+    B, N = parents.shape
+    if masks_out is None:
+        masks_out = torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device=parents.device)
+    _check(load().kdt_tree_verify_prepare(_ptr(parents), _ptr(masks_out), _ptr(cache_lens), ctypes.byref(desc),
+                                          _ptr(workspace), workspace.numel(), _ptr(dev_status), _stream(stream)))
+    return masks_out
 
 
 def attend(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, bitmask, scale, out, desc: VerifyDesc, workspace,

@@ -266,6 +266,25 @@ int kdt_tree_verify_plan(const int32_t *cache_lens, const kdt_verify_desc *desc,
     return ok();
 }
 
+int kdt_tree_verify_prepare(const int32_t *parents, uint64_t *bitmask, const int32_t *cache_lens,
+                            const kdt_verify_desc *desc, void *workspace, size_t workspace_bytes,
+                            int32_t *dev_status, void *stream) {
+    if (!parents || !bitmask || !cache_lens)
+        return fail(KDT_ERR_INVALID_ARG, "parents, bitmask and cache_lens must not be NULL");
+    if (((uintptr_t)parents & 3u) || ((uintptr_t)bitmask & 7u) || ((uintptr_t)cache_lens & 3u))
+        return fail(KDT_ERR_MISALIGNED, "parents and cache_lens must be 4-byte and bitmask 8-byte aligned");
+    kdt::Geometry g;
+    int rc = geometry_for(desc, &g);
+    if (rc) return rc;
+    if (desc->batch > INT32_MAX / 2) return fail(KDT_ERR_INVALID_ARG, "batch too large for one launch");
+    rc = check_ws(g, workspace, workspace_bytes);
+    if (rc) return rc;
+    const hipError_t e = kdt::launch_prepare(parents, bitmask, cache_lens, *desc, g, workspace, dev_status,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prepare launch");
+    return ok();
+}
+
 int kdt_tree_verify_attend(const void *q_lat, const void *q_rope, const void *ckv_cache, const void *krope_cache,
                            const void *tree_ckv, const void *tree_krope, const uint64_t *bitmask, float scale,
                            float *out, const kdt_verify_desc *desc, void *workspace, size_t workspace_bytes,

@@ -73,6 +73,9 @@ hipError_t launch_visibility(const int32_t *parents, int B, int N, uint64_t *mas
                              int32_t *dev_status, hipStream_t st);
 hipError_t launch_plan(const int32_t *cache_lens, const kdt_verify_desc &d, const Geometry &g,
                        void *ws, int32_t *dev_status, hipStream_t st);
+hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t *cache_lens,
+                          const kdt_verify_desc &d, const Geometry &g, void *ws, int32_t *dev_status,
+                          hipStream_t st);
 hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units,
                          hipStream_t st);
 hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st);

@@ -29,6 +29,7 @@
 //   * Small batches split the committed keys over workgroups; partial (O, max, sum) are
 //     merged by a log-sum-exp combine.
 #include "kdt_internal.h"
+#include "visibility_rows.h"
 
 namespace kdt {
 
@@ -73,12 +74,34 @@ __device__ __forceinline__ int splits_of(int L, int64_t chunk, int S) {
 constexpr int kXcds = 8;
 constexpr int kMaxSortGroups = 2048;    // above this the groups keep request order
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ cache_lens, int B, int N,
-                                                    int64_t max_len, int64_t total_len, int RT, int S,
-                                                    int64_t chunk, int64_t U, WsHeader *hdr,
-                                                    int64_t *offsets, int32_t *lens, int64_t *gwork,
-                                                    int32_t *gorder, Unit *units, int32_t *dev_status) {
-    __shared__ int s_ok;
+struct PlanArgs {
+    const int32_t *cache_lens;
+    int B, N;
+    int64_t max_len, total_len;
+    int RT, S;
+    int64_t chunk, U;
+    WsHeader *hdr;
+    int64_t *offsets;
+    int32_t *lens;
+    int64_t *gwork;
+    int32_t *gorder;
+    Unit *units;
+    int32_t *dev_status;
+};
+
+// The plan, by one workgroup of any size.
+__device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds) {
+    const int32_t *__restrict__ cache_lens = pa.cache_lens;
+    const int B = pa.B, N = pa.N, RT = pa.RT, S = pa.S;
+    const int64_t max_len = pa.max_len, total_len = pa.total_len, chunk = pa.chunk, U = pa.U;
+    WsHeader *hdr = pa.hdr;
+    int64_t *offsets = pa.offsets;
+    int32_t *lens = pa.lens;
+    int64_t *gwork = pa.gwork;
+    int32_t *gorder = pa.gorder;
+    Unit *units = pa.units;
+    int32_t *dev_status = pa.dev_status;
+    int &s_ok = *s_ok_lds;
     const int tid = threadIdx.x, nth = blockDim.x;
     if (tid == 0) s_ok = 1;
     __syncthreads();
@@ -144,6 +167,24 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ 
         units[x + kXcds * (round * RT + rt)] =
             Unit{b, rt, sp, splits_of(lens[b], chunk, S), (int32_t)k0, (int32_t)k1, offsets[b] + k0};
     }
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs pa) {
+    __shared__ int s_ok;
+    plan_body(pa, &s_ok);
+}
+
+// Masks and plan in one launch (they are independent): workgroups 0 .. B-1 build the masks
+// of one request each, workgroup B runs the plan.  Saves a kernel launch per verify step.
+template <int W>
+__global__ __launch_bounds__(256) void prepare_kernel(const int32_t *__restrict__ parents,
+                                                      uint64_t *__restrict__ masks, PlanArgs pa) {
+    __shared__ int32_t par[kMaxNodes];
+    __shared__ int s_ok;
+    if ((int)blockIdx.x < pa.B)
+        visibility_rows<W>(parents, pa.N, masks, pa.dev_status, blockIdx.x, par);
+    else
+        plan_body(pa, &s_ok);
 }
 
 // ------------------------------------------------------------------------------ attention
@@ -976,14 +1017,46 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------ launchers
+static PlanArgs plan_args(const int32_t *cache_lens, const kdt_verify_desc &d, const Geometry &g, void *ws,
+                          int32_t *dev_status) {
+    char *w = (char *)ws;
+    PlanArgs pa;
+    pa.cache_lens = cache_lens;
+    pa.B = d.batch;
+    pa.N = d.num_nodes;
+    pa.max_len = d.max_cache_len;
+    pa.total_len = d.total_cache_len;
+    pa.RT = g.row_tiles;
+    pa.S = g.nsplit;
+    pa.chunk = g.chunk;
+    pa.U = g.units;
+    pa.hdr = (WsHeader *)(w + g.off_header);
+    pa.offsets = (int64_t *)(w + g.off_offsets);
+    pa.lens = (int32_t *)(w + g.off_lens);
+    pa.gwork = (int64_t *)(w + g.off_gwork);
+    pa.gorder = (int32_t *)(w + g.off_gorder);
+    pa.units = (Unit *)(w + g.off_units);
+    pa.dev_status = dev_status;
+    return pa;
+}
+
 hipError_t launch_plan(const int32_t *cache_lens, const kdt_verify_desc &d, const Geometry &g, void *ws,
                        int32_t *dev_status, hipStream_t st) {
-    char *w = (char *)ws;
-    plan_kernel<<<1, 1024, 0, st>>>(cache_lens, d.batch, d.num_nodes, d.max_cache_len, d.total_cache_len,
-                                    g.row_tiles, g.nsplit, g.chunk, g.units, (WsHeader *)(w + g.off_header),
-                                    (int64_t *)(w + g.off_offsets), (int32_t *)(w + g.off_lens),
-                                    (int64_t *)(w + g.off_gwork), (int32_t *)(w + g.off_gorder),
-                                    (Unit *)(w + g.off_units), dev_status);
+    plan_kernel<<<1, 1024, 0, st>>>(plan_args(cache_lens, d, g, ws, dev_status));
+    return hipGetLastError();
+}
+
+hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t *cache_lens,
+                          const kdt_verify_desc &d, const Geometry &g, void *ws, int32_t *dev_status,
+                          hipStream_t st) {
+    const PlanArgs pa = plan_args(cache_lens, d, g, ws, dev_status);
+    const unsigned grid = (unsigned)d.batch + 1;
+    switch ((d.num_nodes + 63) / 64) {
+        case 1: prepare_kernel<1><<<grid, 256, 0, st>>>(parents, masks, pa); break;
+        case 2: prepare_kernel<2><<<grid, 256, 0, st>>>(parents, masks, pa); break;
+        case 3: prepare_kernel<3><<<grid, 256, 0, st>>>(parents, masks, pa); break;
+        default: prepare_kernel<4><<<grid, 256, 0, st>>>(parents, masks, pa); break;
+    }
     return hipGetLastError();
 }
 
