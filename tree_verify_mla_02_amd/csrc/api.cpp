@@ -193,7 +193,7 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     x.off_units = take(sizeof(kdt::Unit) * (size_t)x.units);
     if (S > 1) {
         x.off_ml = take(8 * (size_t)B * S * x.rows);
-        x.off_o = take(4 * (size_t)B * S * x.rows * d.d_latent);
+        x.off_o = take(4 * (size_t)B * S * rt * kRowsPerTile * d.d_latent);   // whole row tiles
     } else {
         x.off_ml = x.off_o = 0;
     }

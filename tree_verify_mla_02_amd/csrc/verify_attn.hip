@@ -919,101 +919,125 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
                 *(float4 *)(dst + t16 * 32 + g * 8 + 4 * half) = v;
             }
     } else {
+        // Partials keep the wave's register order: block ((b*S + s)*RT + rt)*4 + wave holds the
+        // wave's 32 rows, and the float4 (t16, g) of lane l sits at ((t16*4 + g)*64 + l)*4, so
+        // every store instruction writes 1 KB contiguous (the row-major order would write 32
+        // rows x 32 bytes).  The combine reads the same order.
         const int64_t prow = ((int64_t)b * a.S + s) * R + r;
-        float *dst = a.part_o + prow * DC;
+        const int64_t blk = (((int64_t)b * a.S + s) * a.RT + rt) * kWaves + wave;
+        float *dst = a.part_o + blk * (kRowsPerWave * DC) + lane * 4;
 #pragma unroll
         for (int t16 = 0; t16 < NT16; t16++)
 #pragma unroll
             for (int g = 0; g < 4; g++)
-                *(float4 *)(dst + t16 * 32 + g * 8 + 4 * half) =
+                *(float4 *)(dst + (t16 * 4 + g) * 256) =
                     make_float4(o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2], o[t16][4 * g + 3]);
         if (half == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
     }
 }
 
-// Reductions over the 64 lanes of a wave (butterfly).
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-    return x;
-}
-
 // ------------------------------------------------------------------------------ combine
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, for rows of split
-// requests.  One wave per row; lane handles 8 consecutive output columns.
-template <int DC>
+// requests.  A tile is (request, 32-row group, 32-column tile).  Lane l holds row l % 32 and
+// columns 4*(l/32) + 8g .. +3 of the tile (g = 0..3) -- the attention wave's register order,
+// so each partial load is 1 KB contiguous.  Splits are merged with a running max, U of them in
+// flight.  With WS = 1 each wave of a workgroup takes its own tile; with WS = 4 (many splits)
+// the four waves share one tile, wave w taking splits w, w+4, ..., and their results are
+// merged in LDS.
+template <int DC, int WS>
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (int64_t)a.B * a.R) return;
-    const int b = (int)(row / a.R);
-    const int64_t r = row - (int64_t)b * a.R;
+    constexpr int NT16 = DC / 32;
+    __shared__ float s_m[WS][64], s_den[WS][64], s_acc[WS][16][64];
+    const int lane = threadIdx.x & 63, half = lane >> 5;
+    const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wv = WS == 1 ? 0 : wave_id;             // position among the waves sharing the tile
+    const int64_t groups = (a.R + kRowsPerWave - 1) / kRowsPerWave;     // 32-row groups per request
+    const int64_t tile = WS == 1 ? (int64_t)blockIdx.x * kWaves + wave_id : (int64_t)blockIdx.x;
+    if (tile >= (int64_t)a.B * groups * NT16) return;
+    const int t16 = (int)(tile % NT16);
+    const int64_t grp = (tile / NT16) % groups;
+    const int b = (int)(tile / (NT16 * groups));
     const int ok = a.hdr->ok;                         // both loads in flight together
     const int sb = splits_of(a.lens[b], a.chunk, a.S);
-    if (!ok || sb <= 1) return;
-    const int64_t prow0 = (int64_t)b * a.S * a.R + r;
-    // (max, sum) of split s sits in lane s % 64: the row max M and the denominator are wave
-    // reductions, and split s's weight 2^(m_s - M) is broadcast from its lane.
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < sb; s0 += 64)
-        if (s0 + lane < sb) M = fmaxf(M, a.part_ml[prow0 + (int64_t)(s0 + lane) * a.R].x);
-    M = wave_max(M);
-    constexpr int PER = DC / 64;                      // output columns per lane
-    static_assert(PER == 8 || PER == 1, "columns per lane");
-    float acc[PER];
+    if (!ok || sb <= 1) return;                       // uniform over the workgroup
+    const int64_t r = grp * kRowsPerWave + (lane & 31);
+    const bool valid = r < a.R;
+    const int64_t rc = valid ? r : a.R - 1;
+    const int rt = (int)(grp / kWaves), wave = (int)(grp % kWaves);
+    float acc[4][4];
 #pragma unroll
-    for (int k = 0; k < PER; k++) acc[k] = 0.f;
-    float den = 0.f;
-    if (M != -INFINITY) {
-        for (int s0 = 0; s0 < sb; s0 += 64) {
-            float w = 0.f;
-            if (s0 + lane < sb) {
-                const float2 ml = a.part_ml[prow0 + (int64_t)(s0 + lane) * a.R];
-                w = __builtin_amdgcn_exp2f(ml.x - M);
-                den += w * ml.y;
-            }
-            const int n = sb - s0 < 64 ? sb - s0 : 64;
-            constexpr int U = 4;                      // splits whose rows are in flight together
-            for (int s = 0; s < n; s += U) {
-                float xs[U][PER];
+    for (int g = 0; g < 4; g++)
 #pragma unroll
-                for (int u = 0; u < U; u++) {
-                    if (s + u < n) {
-                        const float *src = a.part_o + (prow0 + (int64_t)(s0 + s + u) * a.R) * DC + lane * PER;
-                        if constexpr (PER == 8) {
-                            const float4 x0 = ((const float4 *)src)[0], x1 = ((const float4 *)src)[1];
-                            xs[u][0] = x0.x; xs[u][1] = x0.y; xs[u][2] = x0.z; xs[u][3] = x0.w;
-                            xs[u][4] = x1.x; xs[u][5] = x1.y; xs[u][6] = x1.z; xs[u][7] = x1.w;
-                        } else {
-                            xs[u][0] = src[0];
-                        }
-                    }
-                }
+        for (int j = 0; j < 4; j++) acc[g][j] = 0.f;
+    float M = -INFINITY, den = 0.f;
+    constexpr int U = 8;                              // splits in flight per wave
+    for (int s0 = wv; s0 < sb; s0 += U * WS) {
+        float2 ml[U];
+        float4 x[U][4];
 #pragma unroll
-                for (int u = 0; u < U; u++) {
-                    if (s + u < n) {
-                        const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), s + u));
+        for (int u = 0; u < U; u++) {
+            const int sp = s0 + u * WS;
+            if (sp < sb) {
+                ml[u] = a.part_ml[((int64_t)b * a.S + sp) * a.R + rc];
+                const int64_t blk = (((int64_t)b * a.S + sp) * a.RT + rt) * kWaves + wave;
+                const float *src = a.part_o + blk * (kRowsPerWave * DC) + lane * 4;
 #pragma unroll
-                        for (int k = 0; k < PER; k++) acc[k] += ws * xs[u][k];
-                    }
-                }
+                for (int g = 0; g < 4; g++) x[u][g] = *(const float4 *)(src + (t16 * 4 + g) * 256);
             }
         }
-        den = wave_sum(den);
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            if (s0 + u * WS < sb && ml[u].x != -INFINITY) {   // a split with no visible key adds nothing
+                const float mn = fmaxf(M, ml[u].x);
+                const float c = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mn);
+                const float w = __builtin_amdgcn_exp2f(ml[u].x - mn);
+                den = den * c + w * ml[u].y;
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    acc[g][0] = acc[g][0] * c + w * x[u][g].x;
+                    acc[g][1] = acc[g][1] * c + w * x[u][g].y;
+                    acc[g][2] = acc[g][2] * c + w * x[u][g].z;
+                    acc[g][3] = acc[g][3] * c + w * x[u][g].w;
+                }
+                M = mn;
+            }
+        }
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    float *dst = a.out + row * DC + lane * PER;
-    if constexpr (PER == 8) {
-        ((float4 *)dst)[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-        ((float4 *)dst)[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-    } else {
-        dst[0] = acc[0] * inv;
+    float tot = den, o[16];
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) o[4 * g + j] = acc[g][j];
+    if constexpr (WS > 1) {
+        s_m[wv][lane] = M;
+        s_den[wv][lane] = den;
+#pragma unroll
+        for (int k = 0; k < 16; k++) s_acc[wv][k][lane] = o[k];
+        __syncthreads();
+        if (wv != 0) return;
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < WS; w++) Mx = fmaxf(Mx, s_m[w][lane]);
+        tot = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; k++) o[k] = 0.f;
+        if (Mx != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < WS; w++) {
+                const float mw = s_m[w][lane];
+                const float c = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
+                tot += c * s_den[w][lane];
+#pragma unroll
+                for (int k = 0; k < 16; k++) o[k] += c * s_acc[w][k][lane];
+            }
+        }
     }
+    if (!valid) return;
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    float *dst = a.out + ((int64_t)b * a.R + r) * DC + t16 * 32 + 4 * half;
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+        *(float4 *)(dst + 8 * g) = make_float4(o[4 * g] * inv, o[4 * g + 1] * inv, o[4 * g + 2] * inv, o[4 * g + 3] * inv);
 }
 
 // ------------------------------------------------------------------------------ launchers
@@ -1074,14 +1098,19 @@ hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype,
 }
 
 hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st) {
-    const int64_t rows = (int64_t)a.B * a.R;
-    const unsigned grid = (unsigned)((rows + 3) / 4);
-    if (d_latent == 512)
-        combine_kernel<512><<<grid, 256, 0, st>>>(a);
-    else if (d_latent == 64)
-        combine_kernel<64><<<grid, 256, 0, st>>>(a);
-    else
+    const int64_t tiles = (int64_t)a.B * ((a.R + kRowsPerWave - 1) / kRowsPerWave) * (d_latent / 32);
+    // many splits: four waves share a tile; otherwise one wave per tile
+    const bool share = a.S >= 16;
+    const unsigned grid = (unsigned)(share ? tiles : (tiles + kWaves - 1) / kWaves);
+    if (d_latent == 512) {
+        if (share) combine_kernel<512, 4><<<grid, 256, 0, st>>>(a);
+        else combine_kernel<512, 1><<<grid, 256, 0, st>>>(a);
+    } else if (d_latent == 64) {
+        if (share) combine_kernel<64, 4><<<grid, 256, 0, st>>>(a);
+        else combine_kernel<64, 1><<<grid, 256, 0, st>>>(a);
+    } else {
         return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
