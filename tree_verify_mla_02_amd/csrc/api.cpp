@@ -139,7 +139,7 @@ kdt::AttnArgs make_args(const kdt_verify_desc &d, const kdt::Geometry &g, void *
     a.lens = (const int32_t *)(w + g.off_lens);
     a.units = (const kdt::Unit *)(w + g.off_units);
     a.part_ml = g.off_ml ? (float2 *)(w + g.off_ml) : nullptr;
-    a.part_o = g.off_o ? (float *)(w + g.off_o) : nullptr;
+    a.part_o = g.off_o ? (uint32_t *)(w + g.off_o) : nullptr;
     return a;
 }
 
@@ -193,7 +193,7 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     x.off_units = take(sizeof(kdt::Unit) * (size_t)x.units);
     if (S > 1) {
         x.off_ml = take(8 * (size_t)B * S * x.rows);
-        x.off_o = take(4 * (size_t)B * S * rt * kRowsPerTile * d.d_latent);   // whole row tiles
+        x.off_o = take(3 * (size_t)B * S * rt * kRowsPerTile * d.d_latent);   // whole row tiles, 24-bit
     } else {
         x.off_ml = x.off_o = 0;
     }

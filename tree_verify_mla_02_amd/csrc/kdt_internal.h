@@ -66,8 +66,8 @@ struct AttnArgs {
     const int32_t *lens;
     const Unit *units;     // one per grid slot
     float2 *part_ml;       // [B][S][R] (running max in log2 domain, sum)
-    float *part_o;         // un-normalised partial outputs, per wave in register order: block
-                           // ((b*S + s)*RT + rt)*4 + wave of 32 rows x d_c
+    uint32_t *part_o;      // un-normalised partial outputs as packed 24-bit floats, per wave
+                           // in register order: block ((b*S + s)*RT + rt)*4 + wave of 32 rows x d_c
 };
 
 hipError_t launch_visibility(const int32_t *parents, int B, int N, uint64_t *masks,

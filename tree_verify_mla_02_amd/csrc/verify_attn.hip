@@ -649,6 +649,27 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const u
     });
 }
 
+// Split partials are stored as 24-bit floats: the top 24 bits of the fp32 value (sign,
+// exponent, 15 mantissa bits) rounded to nearest even -- relative error <= 2^-17, far inside
+// the output tolerance -- 4 values in 3 words.  The partial round trip through memory (the
+// cost of splitting keys over workgroups) is a quarter smaller.
+__device__ __forceinline__ uint32_t to24(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ float from24(uint32_t v) { return __uint_as_float(v << 8); }
+__device__ __forceinline__ void pack24x4(uint32_t *dst, float a, float b, float c, float d) {
+    const uint32_t x = to24(a), y = to24(b), z = to24(c), w = to24(d);
+    dst[0] = x | (y << 24);
+    dst[1] = (y >> 8) | (z << 16);
+    dst[2] = (z >> 16) | (w << 8);
+}
+__device__ __forceinline__ float4 unpack24x4(const uint32_t *src) {
+    const uint32_t p = src[0], q = src[1], r = src[2];
+    return make_float4(from24(p & 0xffffffu), from24((p >> 24) | ((q & 0xffffu) << 8)),
+                       from24((q >> 16) | ((r & 0xffu) << 16)), from24(r >> 8));
+}
+
 template <typename T, int DC, int DR>
 __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     using Sh = Shape<T, DC, DR>;
@@ -920,18 +941,18 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             }
     } else {
         // Partials keep the wave's register order: block ((b*S + s)*RT + rt)*4 + wave holds the
-        // wave's 32 rows, and the float4 (t16, g) of lane l sits at ((t16*4 + g)*64 + l)*4, so
-        // every store instruction writes 1 KB contiguous (the row-major order would write 32
-        // rows x 32 bytes).  The combine reads the same order.
+        // wave's 32 rows, and the 4 values (t16, g) of lane l, packed to 3 words, sit at words
+        // ((t16*4 + g)*64 + l)*3, so every store instruction writes 768 contiguous bytes (the
+        // row-major order would write 32 rows x 32 bytes).  The combine reads the same order.
         const int64_t prow = ((int64_t)b * a.S + s) * R + r;
         const int64_t blk = (((int64_t)b * a.S + s) * a.RT + rt) * kWaves + wave;
-        float *dst = a.part_o + blk * (kRowsPerWave * DC) + lane * 4;
+        uint32_t *dst = a.part_o + blk * (kRowsPerWave * DC / 4 * 3) + lane * 3;
 #pragma unroll
         for (int t16 = 0; t16 < NT16; t16++)
 #pragma unroll
             for (int g = 0; g < 4; g++)
-                *(float4 *)(dst + (t16 * 4 + g) * 256) =
-                    make_float4(o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2], o[t16][4 * g + 3]);
+                pack24x4(dst + (t16 * 4 + g) * 192, o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2],
+                         o[t16][4 * g + 3]);
         if (half == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
     }
 }
@@ -940,7 +961,7 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, for rows of split
 // requests.  A tile is (request, 32-row group, 32-column tile).  Lane l holds row l % 32 and
 // columns 4*(l/32) + 8g .. +3 of the tile (g = 0..3) -- the attention wave's register order,
-// so each partial load is 1 KB contiguous.  Splits are merged with a running max, U of them in
+// so each partial load (4 packed values per lane) is 768 bytes contiguous.  Splits are merged with a running max, U of them in
 // flight.  With WS = 1 each wave of a workgroup takes its own tile; with WS = 4 (many splits)
 // the four waves share one tile, wave w taking splits w, w+4, ..., and their results are
 // merged in LDS.
@@ -980,9 +1001,9 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
             if (sp < sb) {
                 ml[u] = a.part_ml[((int64_t)b * a.S + sp) * a.R + rc];
                 const int64_t blk = (((int64_t)b * a.S + sp) * a.RT + rt) * kWaves + wave;
-                const float *src = a.part_o + blk * (kRowsPerWave * DC) + lane * 4;
+                const uint32_t *src = a.part_o + blk * (kRowsPerWave * DC / 4 * 3) + lane * 3;
 #pragma unroll
-                for (int g = 0; g < 4; g++) x[u][g] = *(const float4 *)(src + (t16 * 4 + g) * 256);
+                for (int g = 0; g < 4; g++) x[u][g] = unpack24x4(src + (t16 * 4 + g) * 192);
             }
         }
 #pragma unroll
