@@ -566,59 +566,68 @@ __device__ __forceinline__ void ds_read_k(bf16x8 &dst, const LDS_AS char *base) 
     asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(base), "i"(OFF));
 }
 
-// S^T for 32 keys (block KB of the tile) x this wave's 32 rows: NQ MFMA 32x32x16.  The K
-// fragment of step kk is read QD steps ahead into slot kk % (QD+1), so a slot is refilled
-// one MFMA after the one that last read it.
-template <class Sh, int NQ, int KB, class F>
-__device__ __forceinline__ f32x16 qk_block(const LDS_AS char *buf, const bf16x8 (&q)[NQ],
-                                           const int (&qk_base)[Sh::CB / 2], F &&fill) {
+// S^T of both 32-key blocks of a tile x this wave's 32 rows: one chain of 2*NQ MFMA 32x32x16,
+// block 0's accumulator first, then block 1's.  The K fragment of step g is read QD steps
+// ahead into slot g % (QD+1) -- across the block boundary too, so block 1 starts without
+// refilling the pipeline -- and a slot is refilled one MFMA after the one that last read it.
+// mid() runs once block 0's scores are final, before the first fill; fill(K) runs after
+// block 1's MFMA K.
+template <class Sh, int NQ, class Mid, class F>
+__device__ __forceinline__ void qk_pair(const LDS_AS char *buf, const bf16x8 (&q)[NQ],
+                                        const int (&qk_base)[Sh::CB / 2], f32x16 &s0, f32x16 &s1, Mid &&mid,
+                                        F &&fill) {
     constexpr int PAT = Sh::CB / 2;
+    constexpr int NG = 2 * NQ;
     constexpr int QD = NQ > 5 ? 5 : NQ - 1, NS = QD + 1;
-    static_assert(QD >= 1, "chain of at least two MFMAs");
+    static_assert(QD >= 1, "chain of at least two MFMAs per block");
     const LDS_AS char *pq[PAT];
 #pragma unroll
     for (int j = 0; j < PAT; j++) pq[j] = buf + qk_base[j];
     bf16x8 kf[NS];
-    static_for<0, QD>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        ds_read_k<key_off<Sh>(KB * 32) + (j / PAT) * 1024>(kf[j % NS], pq[j % PAT]);
-    });
-    f32x16 acc;
-    static_for<0, NQ>([&](auto KK) {
-        constexpr int kk = decltype(KK)::value;
-        // loads issued so far: steps < min(NQ, kk + QD); those after step kk may stay in flight
-        constexpr int issued = (kk + QD < NQ) ? kk + QD : NQ;
-        constexpr int after = issued - kk - 1;
+    auto read = [&](auto G) {
+        constexpr int g = decltype(G)::value, kb = g / NQ, kk = g % NQ;
+        ds_read_k<key_off<Sh>(kb * 32) + (kk / PAT) * 1024>(kf[g % NS], pq[kk % PAT]);
+    };
+    static_for<0, QD>(read);
+    static_for<0, NG>([&](auto G) {
+        constexpr int g = decltype(G)::value, kb = g / NQ, kk = g % NQ;
+        // loads issued so far: steps < min(NG, g + QD); those after step g may stay in flight
+        constexpr int issued = (g + QD < NG) ? g + QD : NG;
+        constexpr int after = issued - g - 1;
+        f32x16 &acc = kb == 0 ? s0 : s1;
         if constexpr (kk == 0)
-            mfma_s_first<after>(acc, kf[0], q[0]);
+            mfma_s_first<after>(acc, kf[g % NS], q[kk]);
         else if constexpr (kk == NQ - 1)
-            mfma_s_last<after>(acc, kf[kk % NS], q[kk]);
+            mfma_s_last<after>(acc, kf[g % NS], q[kk]);
         else
-            mfma_s_next<after>(acc, kf[kk % NS], q[kk]);
-        if constexpr (kk + QD < NQ) {
-            constexpr int n = kk + QD;
-            ds_read_k<key_off<Sh>(KB * 32) + (n / PAT) * 1024>(kf[n % NS], pq[n % PAT]);
+            mfma_s_next<after>(acc, kf[g % NS], q[kk]);
+        if constexpr (g + QD < NG) read(IntC<g + QD>{});
+        if constexpr (kb == 1) {
+            if constexpr (kk == 0) mid();
+            fill(IntC<kk>{});                      // independent work for the MFMA shadow
         }
-        fill(KK);                                  // independent work for the MFMA shadow
         __builtin_amdgcn_sched_barrier(0);         // keep each step's instructions together
     });
-    return acc;
 }
 
-// O^T += V^T P^T for 32 keys (block kb): for each 16-key step and 32-column tile, one V^T
-// fragment (two ds_read_b64_tr_b16) feeds the hi and the lo MFMA.  Fragments are read PD
-// steps ahead; column tiles go in pairs so consecutive MFMAs use different accumulators.
-// fill(m) runs after MFMA m (0 .. 4*NT16-1): work issued there overlaps the matrix core.  P
-// is read at the MFMA that uses it, so fill may still be producing keys 16..31 (phi[1], plo[1])
-// during the first half of the chain.
-template <class Sh, int NT16, class F>
-__device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const u32x4 (&phi)[2],
-                                         const u32x4 (&plo)[2], f32x16 (&o)[NT16],
-                                         const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1][2], F &&fill) {
-    constexpr int NSTEP = 2 * NT16;     // (h16, t16) pairs
+// O^T += V^T P^T over both 32-key blocks of a tile: one chain of 2 x 4*NT16 MFMAs.  For each
+// 16-key step and 32-column tile, one V^T fragment (two ds_read_b64_tr_b16) feeds the hi and
+// the lo MFMA.  Fragments are read PD steps ahead -- across the block boundary too, so block 1
+// starts without refilling the pipeline; column tiles go in pairs so consecutive MFMAs use
+// different accumulators.  mid() runs between the blocks (after block 0's last MFMA, before
+// block 1's first); fill(m) runs after MFMA m (0 .. 8*NT16-1).  P is read at the MFMA that
+// uses it, so fill may still be producing keys 16..31 of a block during the first half of
+// that block's MFMAs.
+template <class Sh, int NT16, class Mid, class F>
+__device__ __forceinline__ void pv_pair(const LDS_AS char *buf, const u32x4 (&phi0)[2], const u32x4 (&plo0)[2],
+                                        const u32x4 (&phi1)[2], const u32x4 (&plo1)[2], f32x16 (&o)[NT16],
+                                        const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1][2], Mid &&mid,
+                                        F &&fill) {
+    constexpr int NSTEP = 2 * NT16;     // (h16, t16) pairs per block
     constexpr int PD = 4;
     auto load = [&](int st) {
-        const int h16 = st / NT16, t16 = st % NT16;
+        const int kb = st / NSTEP, sl = st % NSTEP;
+        const int h16 = sl / NT16, t16 = sl % NT16;
         const int kbase = kb * 32 + 16 * h16;
         const int j = (4 * t16 % Sh::CB) / 4, cg_off = (4 * t16 / Sh::CB) * 1024 + key_off<Sh>(kbase);
         const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(buf + pv_base[j][0] + cg_off));
@@ -629,9 +638,16 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const u
 #pragma unroll
     for (int j = 0; j < PD; j++) vf[j] = load(j);
     __builtin_amdgcn_sched_barrier(0);
-    static_for<0, NSTEP / 2>([&](auto S2) {
+    static_for<0, NSTEP>([&](auto S2) {     // NSTEP pairs of steps over the two blocks
         constexpr int st = 2 * decltype(S2)::value;
-        constexpr int h16 = st / NT16, t16 = st % NT16, m = 2 * st;
+        constexpr int kb = st / NSTEP, sl = st % NSTEP;
+        constexpr int h16 = sl / NT16, t16 = sl % NT16, m = 2 * st;
+        const u32x4(&phi)[2] = kb == 0 ? phi0 : phi1;
+        const u32x4(&plo)[2] = kb == 0 ? plo0 : plo1;
+        if constexpr (sl == 0 && kb == 1) {
+            mid();
+            __builtin_amdgcn_sched_barrier(0);
+        }
         o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], __builtin_bit_cast(bf16x8, phi[h16]), o[t16], 0, 0, 0);
         fill(IntC<m>{});
         __builtin_amdgcn_sched_barrier(0);
@@ -639,11 +655,11 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *buf, int kb, const u
         fill(IntC<m + 1>{});
         __builtin_amdgcn_sched_barrier(0);
         o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], __builtin_bit_cast(bf16x8, plo[h16]), o[t16], 0, 0, 0);
-        if constexpr (st + PD < NSTEP) vf[st % PD] = load(st + PD);
+        if constexpr (st + PD < 2 * NSTEP) vf[st % PD] = load(st + PD);
         fill(IntC<m + 2>{});
         __builtin_amdgcn_sched_barrier(0);
         o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], __builtin_bit_cast(bf16x8, plo[h16]), o[t16 + 1], 0, 0, 0);
-        if constexpr (st + 1 + PD < NSTEP) vf[(st + 1) % PD] = load(st + 1 + PD);
+        if constexpr (st + 1 + PD < 2 * NSTEP) vf[(st + 1) % PD] = load(st + 1 + PD);
         fill(IntC<m + 3>{});
         __builtin_amdgcn_sched_barrier(0);
     });
@@ -834,8 +850,8 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             // BlockSm).  The first half of a block's softmax (maxima, reference update, keys
             // 0..15) must be done before its P.V chain starts; the second half (keys 16..31)
             // only before the chain's MFMA 2*NT16, so it runs in the first slots of that chain.
-            //   QK0                                   (LDS-bound: nothing else)
-            //   QK1: block 0, first half
+            //   QK0, QK1 (one chain)                  QK1 slots: block 0, first half
+            //                                         (QK0 is LDS-bound: nothing else)
             //   P.V0: block 0 second half | block 1 first half | copy set-up | copies 0..NINST/2
             //   P.V1: block 1 second half | copies NINST/2..NINST
             // The copy of tile t+1 goes into P.V chains (which leave LDS bandwidth to spare for
@@ -847,12 +863,10 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             constexpr int H1 = kSmPre + 16;                 // steps of a softmax first half
             constexpr int NC = Dma::NINST;
             BlockSm b0, b1;
-            b0.s = qk_block<Sh, NQ, 0>(buf, q, qk_base, NoFill{});
-            if (need_mask) mask_scores(b0.s, w0);
             using A0 = Spread<0, H1, 0, 1>;
-            b1.s = qk_block<Sh, NQ, 1>(buf, q, qk_base, [&](auto K) {
-                A0::template at<decltype(K)::value, NQ>([&](auto J) { b0.template stage<J.value>(sm); });
-            });
+            qk_pair<Sh, NQ>(
+                buf, q, qk_base, b0.s, b1.s, [&]() { if (need_mask) mask_scores(b0.s, w0); },
+                [&](auto K) { A0::template at<decltype(K)::value, NQ>([&](auto J) { b0.template stage<J.value>(sm); }); });
             A0::template tail<NQ>([&](auto J) { b0.template stage<J.value>(sm); });
             if (need_mask) mask_scores(b1.s, w1);
             if (__ballot(b0.u.alpha != 1.f)) rescale_acc<NT16>(o, b0.u.alpha);
@@ -865,26 +879,33 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             using A1 = Spread<0, H1, kSmStages - H1, 1>;
             constexpr int kSetup = kSmStages;
             using C0 = Spread<0, NC / 2, kSetup + 1, 2>;
-            pv_block<Sh, NT16>(buf, 0, b0.phi, b0.plo, o, pv_base, [&](auto K) {
-                constexpr int k = decltype(K)::value;
-                B0::template at<k, NPVM>([&](auto J) { b0.template stage<J.value>(sm); });
-                A1::template at<k, NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
-                if constexpr (k == kSetup) dma_setup(dn, more ? t + 1 : t, (t + 1) & 1);
-                C0::template at<k, NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
-            });
-            B0::template tail<NPVM>([&](auto J) { b0.template stage<J.value>(sm); });
-            A1::template tail<NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
-            if constexpr (kSetup >= NPVM) dma_setup(dn, more ? t + 1 : t, (t + 1) & 1);
-            C0::template tail<NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
-            if (__ballot(b1.u.alpha != 1.f)) rescale_acc<NT16>(o, b1.u.alpha);
-            if constexpr (!kIn) static_for<H1, kSmStages>([&](auto J) { b1.template stage<J.value>(sm); });
             using B1 = Spread<H1, H1e, 0, 1>;
             using C1 = Spread<NC / 2, NC, kSmStages - H1, 2>;
-            pv_block<Sh, NT16>(buf, 1, b1.phi, b1.plo, o, pv_base, [&](auto K) {
-                constexpr int k = decltype(K)::value;
-                B1::template at<k, NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
-                C1::template at<k, NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
-            });
+            pv_pair<Sh, NT16>(
+                buf, b0.phi, b0.plo, b1.phi, b1.plo, o, pv_base,
+                [&]() {
+                    // what block 0's slots could not hold (block 1's first half, and its second
+                    // half for short chains), then the rare rescale of O for block 1
+                    B0::template tail<NPVM>([&](auto J) { b0.template stage<J.value>(sm); });
+                    A1::template tail<NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
+                    if constexpr (!kIn) static_for<H1, kSmStages>([&](auto J) { b1.template stage<J.value>(sm); });
+                    if constexpr (kSetup >= NPVM) dma_setup(dn, more ? t + 1 : t, (t + 1) & 1);
+                    C0::template tail<NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+                    if (__ballot(b1.u.alpha != 1.f)) rescale_acc<NT16>(o, b1.u.alpha);
+                },
+                [&](auto K) {
+                    constexpr int k = decltype(K)::value;
+                    if constexpr (k < NPVM) {           // block 0's P.V
+                        B0::template at<k, NPVM>([&](auto J) { b0.template stage<J.value>(sm); });
+                        A1::template at<k, NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
+                        if constexpr (k == kSetup) dma_setup(dn, more ? t + 1 : t, (t + 1) & 1);
+                        C0::template at<k, NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+                    } else {                            // block 1's P.V
+                        constexpr int k1 = k - NPVM;
+                        B1::template at<k1, NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
+                        C1::template at<k1, NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
+                    }
+                });
             B1::template tail<NPVM>([&](auto J) { b1.template stage<J.value>(sm); });
             C1::template tail<NPVM>([&](auto J) { dn.template issue<J.value, J.value + 1>(); });
             sm.l = (sm.l * b0.u.alpha + b0.sum) * b1.u.alpha + b1.sum;
