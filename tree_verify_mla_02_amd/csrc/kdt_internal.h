@@ -26,7 +26,9 @@ struct Geometry {
     int row_tiles;         // RT = ceil(R / 128)
     int nsplit;            // S: splits per request at most (1 = no split)
     int64_t chunk;         // committed keys per split
-    int64_t units;         // grid size of the attention kernel: 8 * ceil(B * S / 8) * RT slots
+    int64_t units;         // grid size of the attention kernel: 8 * ceil(G / 8) * bt * bs slots
+    int bt, bs;            // a plan group: bt row tiles x bs splits of one request
+    int64_t groups;        // G = B * ceil(RT / bt) * ceil(S / bs)
     int mask_words;        // W = ceil(N / 64)
     // workspace layout (byte offsets, 256-aligned)
     size_t off_header, off_offsets, off_lens, off_gwork, off_gorder, off_units, off_ml, off_o, total_bytes;

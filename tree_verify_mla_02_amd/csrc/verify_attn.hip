@@ -78,7 +78,7 @@ struct PlanArgs {
     const int32_t *cache_lens;
     int B, N;
     int64_t max_len, total_len;
-    int RT, S;
+    int RT, S, bt, bs;
     int64_t chunk, U;
     WsHeader *hdr;
     int64_t *offsets;
@@ -92,7 +92,7 @@ struct PlanArgs {
 // The plan, by one workgroup of any size.
 __device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds) {
     const int32_t *__restrict__ cache_lens = pa.cache_lens;
-    const int B = pa.B, N = pa.N, RT = pa.RT, S = pa.S;
+    const int B = pa.B, N = pa.N, RT = pa.RT, S = pa.S, bt = pa.bt, bs = pa.bs;
     const int64_t max_len = pa.max_len, total_len = pa.total_len, chunk = pa.chunk, U = pa.U;
     WsHeader *hdr = pa.hdr;
     int64_t *offsets = pa.offsets;
@@ -123,15 +123,22 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds) {
     }
     __syncthreads();
     const int ok = s_ok;
-    const int64_t G = (int64_t)B * S;
-    // work of group (b, s): its cache keys plus the tree keys for split 0; -1 = no such split
+    // Groups: bt row tiles x bs splits of one request, (request, row-tile block, split block)
+    // with the split block fastest.  Work = the keys of its splits (the row tiles all cost the
+    // same); -1 = no such split anywhere in the block (or rejected lengths).
+    const int GR = (RT + bt - 1) / bt, GS = (S + bs - 1) / bs;
+    const int64_t G = (int64_t)B * GR * GS;
+    const int per = bt * bs;
     for (int64_t g = tid; g < G; g += nth) {
-        const int b = (int)(g / S), sp = (int)(g % S);
+        const int b = (int)(g / ((int64_t)GR * GS)), gs = (int)(g % GS);
         const int L = lens[b];
         int64_t w = -1;
-        if (ok && sp < splits_of(L, chunk, S)) {
-            const int64_t left = (int64_t)L - sp * chunk;
-            w = (left < chunk ? (left > 0 ? left : 0) : chunk) + (sp == 0 ? N : 0);
+        if (ok) {
+            const int sbr = splits_of(L, chunk, S);
+            for (int sp = gs * bs; sp < gs * bs + bs && sp < sbr; sp++) {
+                const int64_t left = (int64_t)L - sp * chunk;
+                w = (w < 0 ? 0 : w) + (left < chunk ? (left > 0 ? left : 0) : chunk) + (sp == 0 ? N : 0);
+            }
         }
         gwork[g] = w;
     }
@@ -151,21 +158,24 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds) {
     }
     __syncthreads();
     // Group p (in work order) goes to XCD lane x in snake order over rounds of 8 groups; its
-    // row tile rt takes grid slot x + 8 * (round * RT + rt).  Slots are dealt to the XCDs
+    // unit i takes grid slot x + 8 * (round * per + i).  Slots are dealt to the XCDs
     // round-robin, so a group runs on one XCD.
-    for (int64_t e = tid; e < G * RT; e += nth) {
-        const int64_t p = e / RT;
-        const int rt = (int)(e % RT);
+    for (int64_t e = tid; e < G * per; e += nth) {
+        const int64_t p = e / per;
+        const int i = (int)(e % per);
         const int g = gorder[p];
         if (gwork[g] < 0) continue;
+        const int b = (int)(g / ((int64_t)GR * GS));
+        const int gr = (int)((g / GS) % GR), gs = (int)(g % GS);
+        const int rt = gr * bt + i / bs, sp = gs * bs + i % bs;
+        const int sb = splits_of(lens[b], chunk, S);
+        if (rt >= RT || sp >= sb) continue;
         const int64_t round = p / kXcds;
         const int j = (int)(p % kXcds);
         const int x = (round & 1) ? kXcds - 1 - j : j;
-        const int b = g / S, sp = g % S;
         const int64_t k0 = (int64_t)sp * chunk;
         const int64_t k1 = k0 + chunk < (int64_t)lens[b] ? k0 + chunk : (int64_t)lens[b];
-        units[x + kXcds * (round * RT + rt)] =
-            Unit{b, rt, sp, splits_of(lens[b], chunk, S), (int32_t)k0, (int32_t)k1, offsets[b] + k0};
+        units[x + kXcds * (round * per + i)] = Unit{b, rt, sp, sb, (int32_t)k0, (int32_t)k1, offsets[b] + k0};
     }
 }
 
@@ -1094,6 +1104,8 @@ static PlanArgs plan_args(const int32_t *cache_lens, const kdt_verify_desc &d, c
     pa.total_len = d.total_cache_len;
     pa.RT = g.row_tiles;
     pa.S = g.nsplit;
+    pa.bt = g.bt;
+    pa.bs = g.bs;
     pa.chunk = g.chunk;
     pa.U = g.units;
     pa.hdr = (WsHeader *)(w + g.off_header);
