@@ -89,8 +89,9 @@ struct PlanArgs {
     int32_t *dev_status;
 };
 
-// The plan, by one workgroup of any size.
-__device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds) {
+// The plan, by one workgroup of any size.  s_work (LDS, kMaxSortGroups entries) holds the
+// group work when it fits, so the rank sort reads LDS rather than global memory.
+__device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds, int64_t *s_work) {
     const int32_t *__restrict__ cache_lens = pa.cache_lens;
     const int B = pa.B, N = pa.N, RT = pa.RT, S = pa.S, bt = pa.bt, bs = pa.bs;
     const int64_t max_len = pa.max_len, total_len = pa.total_len, chunk = pa.chunk, U = pa.U;
@@ -129,6 +130,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds) {
     const int GR = (RT + bt - 1) / bt, GS = (S + bs - 1) / bs;
     const int64_t G = (int64_t)B * GR * GS;
     const int per = bt * bs;
+    int64_t *work = G <= kMaxSortGroups ? s_work : gwork;
     for (int64_t g = tid; g < G; g += nth) {
         const int b = (int)(g / ((int64_t)GR * GS)), gs = (int)(g % GS);
         const int L = lens[b];
@@ -140,17 +142,17 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds) {
                 w = (w < 0 ? 0 : w) + (left < chunk ? (left > 0 ? left : 0) : chunk) + (sp == 0 ? N : 0);
             }
         }
-        gwork[g] = w;
+        work[g] = w;
     }
     for (int64_t u = tid; u < U; u += nth) units[u] = Unit{-1, 0, 0, 0, 0, 0, 0};
     __syncthreads();
     for (int64_t g = tid; g < G; g += nth) {
         int64_t rank = g;
         if (G <= kMaxSortGroups) {      // more work first, ties by index
-            const int64_t w = gwork[g];
+            const int64_t w = work[g];
             rank = 0;
             for (int64_t h = 0; h < G; h++) {
-                const int64_t wh = gwork[h];
+                const int64_t wh = work[h];
                 rank += (wh > w) || (wh == w && h < g);
             }
         }
@@ -164,7 +166,7 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds) {
         const int64_t p = e / per;
         const int i = (int)(e % per);
         const int g = gorder[p];
-        if (gwork[g] < 0) continue;
+        if (work[g] < 0) continue;
         const int b = (int)(g / ((int64_t)GR * GS));
         const int gr = (int)((g / GS) % GR), gs = (int)(g % GS);
         const int rt = gr * bt + i / bs, sp = gs * bs + i % bs;
@@ -181,7 +183,8 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds) {
 
 __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs pa) {
     __shared__ int s_ok;
-    plan_body(pa, &s_ok);
+    __shared__ int64_t s_work[kMaxSortGroups];
+    plan_body(pa, &s_ok, s_work);
 }
 
 // Masks and plan in one launch (they are independent): workgroups 0 .. B-1 build the masks
@@ -191,10 +194,11 @@ __global__ __launch_bounds__(256) void prepare_kernel(const int32_t *__restrict_
                                                       uint64_t *__restrict__ masks, PlanArgs pa) {
     __shared__ int32_t par[kMaxNodes];
     __shared__ int s_ok;
+    __shared__ int64_t s_work[kMaxSortGroups];
     if ((int)blockIdx.x < pa.B)
         visibility_rows<W>(parents, pa.N, masks, pa.dev_status, blockIdx.x, par);
     else
-        plan_body(pa, &s_ok);
+        plan_body(pa, &s_ok, s_work);
 }
 
 // ------------------------------------------------------------------------------ attention
