@@ -10,7 +10,8 @@ latent 512 + rope 64, bf16, committed cache 4096 tokens, a 64-node best-first dr
 
 One JSON line is printed.  `value` is algorithmic TFLOP/s of the whole step;
 `roofline` rates the attention kernel alone (HIP events around each of its launches in the
-timed region, on the stream it runs on) against the roof that binds it (bf16 MFMA peak, or
+timed region, on the stream it runs on, recorded without a system-scope cache fence so that
+timing does not add cache write-backs to the step) against the roof that binds it (bf16 MFMA peak, or
 HBM bandwidth when the algorithmic intensity is below the ridge point), with `traffic` the HBM
 bytes per launch from the committed rocprofv3 counter summary (null when the kernel sources
 changed since it was taken); `cpu_baseline` times the fp64 oracle on the host cores.
@@ -34,6 +35,53 @@ import workloads  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X dense fp32 MFMA
 PEAK_HBM_GBPS = 8000.0
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class HipEvents:
+    """Timing events of the HIP runtime the process already runs (torch's), created with
+    hipEventDisableSystemFence: recording one does not write back and invalidate the caches
+    (a default event's system-scope fence does, which between two kernels of a step costs
+    several microseconds, most of it writing back the split partials).  The timestamps still
+    follow the completion of the work recorded before them."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        # by soname: dlopen returns the runtime torch has loaded, not a second copy
+        self.hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.flags = HIP_EVENT_DISABLE_SYSTEM_FENCE
+        self.events = []
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        err = self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.flags)
+        if err != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({err})")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        err = self.hip.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream))
+        if err != 0:
+            raise RuntimeError(f"hipEventRecord failed ({err})")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        err = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if err != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({err})")
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
 
 
 def tree_depth_sum(parents: np.ndarray) -> np.ndarray:
@@ -99,26 +147,28 @@ def run(args):
 
     # ---- timed region: K whole steps; the attention kernel's own launches are bracketed by
     # events on the stream it runs on (the same stream as the rest of the step)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    he = HipEvents()
+    evs = [(he.create(), he.create()) for _ in range(args.steps)]
 
     def timed_step(i):
         kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
-        evs[i][0].record(stream)
+        he.record(evs[i][0], stream)
         kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
-        evs[i][1].record(stream)
+        he.record(evs[i][1], stream)
         kdt.combine(out, desc, ws, stream=stream)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
+    ev0, ev1 = he.create(), he.create()
+    he.record(ev0, stream)
     for i in range(args.steps):
         timed_step(i)
-    ev1.record(stream)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    he.record(ev1, stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
-    step_ms = ev0.elapsed_time(ev1) / args.steps
-    attn_each = np.array([a.elapsed_time(b) for a, b in evs])
+    step_ms = he.elapsed_ms(ev0, ev1) / args.steps
+    attn_each = np.array([he.elapsed_ms(a, b) for a, b in evs])
     attn_ms = float(attn_each.mean())
 
     # ---- cold caches: before each of a few attention launches, write a 512 MiB scratch buffer
@@ -129,14 +179,15 @@ def run(args):
         for _ in range(args.cold_steps):
             scratch.fill_(1)
             kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
+            a0, a1 = he.create(), he.create()
+            he.record(a0, stream)
             kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
-            a1.record(stream)
+            he.record(a1, stream)
             kdt.combine(out, desc, ws, stream=stream)
             torch.cuda.synchronize()
-            cold.append(a0.elapsed_time(a1))
+            cold.append(he.elapsed_ms(a0, a1))
         del scratch
+    he.close()
 
     # the roof that binds: MFMA when the algorithmic intensity is above the ridge point
     mfma_peak = PEAK_BF16_TFLOPS if sp.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -177,6 +228,7 @@ def run(args):
         "arith_intensity_flop_per_byte": round(flops / nbytes, 1),
         "kernel_source_hash": kernel_source_hash(),
         "wall_ms_timed_region": round(wall_ms, 3),
+        "host_launch_ms_per_step": round(host_ms / args.steps, 5),
         "roofline": {
             "bound": bound,
             "achieved": round(achieved, 3),

@@ -74,6 +74,25 @@ __device__ __forceinline__ int splits_of(int L, int64_t chunk, int S) {
 constexpr int kXcds = 8;
 constexpr int kMaxSortGroups = 2048;    // above this the groups keep request order
 
+// Division of 32-bit unsigned integers by a divisor d (1 <= d <= 2^31) fixed for the launch, as
+// a high multiply and shifts (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994): l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+// t = mulhi(m, n), n / d = (t + ((n - t) >> 1)) >> (l - 1), and n / 1 = n.  The host sets the
+// constants; a hardware-less 32-bit division is a dependent chain of about forty instructions.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+static inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while (((uint64_t)1 << l) < d) l++;
+    const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
+    const uint32_t t = __umulhi(n, f.m);
+    return f.l == 0 ? n : (t + ((n - t) >> 1)) >> (f.l - 1);
+}
+
 struct PlanArgs {
     const int32_t *cache_lens;
     int B, N;
@@ -87,104 +106,198 @@ struct PlanArgs {
     int32_t *gorder;
     Unit *units;
     int32_t *dev_status;
+    FastDiv fd_chunk, fd_per, fd_grgs, fd_gs, fd_gr, fd_bs;
 };
 
-// The plan, by one workgroup of any size.  s_work (LDS, kMaxSortGroups entries) holds the
-// group work when it fits, so the rank sort reads LDS rather than global memory.
-__device__ __forceinline__ void plan_body(const PlanArgs &pa, int *s_ok_lds, int64_t *s_work) {
+// LDS of the plan: the lengths and offsets of up to kMaxLdsReq requests, and the group work
+// and order of up to kMaxSortGroups groups, so that every step after the first load of
+// cache_lens reads LDS (larger batches fall back to the workspace copies).
+constexpr int kMaxLdsReq = 1024;
+struct alignas(16) PlanLds {
+    uint32_t key[kMaxSortGroups];       // sort key of each group (see plan_body); 16-byte reads
+    int32_t order[kMaxSortGroups];
+    int64_t offs[kMaxLdsReq];
+    int64_t wsum[16];                   // per-wave totals of the offsets scan (<= 1024 threads)
+    int32_t lens[kMaxLdsReq];
+    int32_t sb[kMaxLdsReq];             // splits of each request
+    int ok;
+};
+static_assert(kMaxSortGroups % 4 == 0, "whole 16-byte key reads");
+
+// Barrier for data exchanged through LDS only: waits for this wave's LDS traffic, not for
+// its global stores (a full __syncthreads also waits for every store to reach memory).
+__device__ __forceinline__ void lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// The plan, by one workgroup whose size is a multiple of 64 (at most 1024).  Index
+// arithmetic is 32-bit: the host bounds the grid (every group index and unit slot) below 2^31,
+// and divides by the launch's fixed divisors through FastDiv.
+__device__ __forceinline__ void plan_body(const PlanArgs &pa, PlanLds &L) {
     const int32_t *__restrict__ cache_lens = pa.cache_lens;
     const int B = pa.B, N = pa.N, RT = pa.RT, S = pa.S, bt = pa.bt, bs = pa.bs;
-    const int64_t max_len = pa.max_len, total_len = pa.total_len, chunk = pa.chunk, U = pa.U;
-    WsHeader *hdr = pa.hdr;
-    int64_t *offsets = pa.offsets;
-    int32_t *lens = pa.lens;
-    int64_t *gwork = pa.gwork;
-    int32_t *gorder = pa.gorder;
-    Unit *units = pa.units;
-    int32_t *dev_status = pa.dev_status;
-    int &s_ok = *s_ok_lds;
-    const int tid = threadIdx.x, nth = blockDim.x;
-    if (tid == 0) s_ok = 1;
-    __syncthreads();
+    const int64_t max_len = pa.max_len, total_len = pa.total_len;
+    const uint32_t chunk = (uint32_t)pa.chunk;
+    const int U = (int)pa.U;
+    const int tid = threadIdx.x, nth = blockDim.x, lane = tid & 63, wave = tid >> 6, nwaves = nth >> 6;
+    const bool req_lds = B <= kMaxLdsReq;
+    int32_t *lens = req_lds ? L.lens : pa.lens;
+    int64_t *offs = req_lds ? L.offs : pa.offsets;
+    // splits of a request of len keys: ceil(len / chunk), at least 1, at most S
+    auto splits = [&](int len) {
+        if (len <= 0) return 1;
+        const uint32_t n = fdiv((uint32_t)len + chunk - 1u, pa.fd_chunk);   // < 2^32
+        return (int)(n < (uint32_t)S ? n : (uint32_t)S);
+    };
+    if (tid == 0) L.ok = 1;
+    lds_sync();
     for (int b = tid; b < B; b += nth) {
-        const int L = cache_lens[b];
-        lens[b] = L;
-        if (L < 0 || (int64_t)L > max_len) s_ok = 0;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int64_t off = 0;
-        for (int b = 0; b < B; b++) {
-            offsets[b] = off;
-            off += lens[b] > 0 ? lens[b] : 0;
+        const int len = cache_lens[b];
+        lens[b] = len;
+        if (req_lds) {
+            pa.lens[b] = len;
+            L.sb[b] = splits(len);
         }
-        if (off > total_len) s_ok = 0;
-        hdr->ok = s_ok;
-        if (!s_ok && dev_status) atomicOr(dev_status, (int32_t)KDT_DEV_CACHE_LEN);
+        if (len < 0 || (int64_t)len > max_len) L.ok = 0;
     }
-    __syncthreads();
-    const int ok = s_ok;
+    if (req_lds) lds_sync(); else __syncthreads();
+    // offsets: exclusive scan of max(len, 0).  Up to 64 requests one thread adds them up
+    // (a chain of adds is shorter than a scan's chain of lane shuffles); more go nth at a
+    // time through wave scans and the wave totals.
+    int64_t carry = 0;
+    if (B <= 64) {
+        if (tid == 0) {
+            for (int b = 0; b < B; b++) {
+                offs[b] = carry;
+                if (req_lds) pa.offsets[b] = carry;
+                carry += lens[b] > 0 ? lens[b] : 0;
+            }
+        }
+    } else {
+        for (int base = 0; base < B; base += nth) {
+            const int b = base + tid;
+            const int64_t v = b < B && lens[b] > 0 ? lens[b] : 0;
+            int64_t x = v;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int64_t y = __shfl_up(x, d, 64);
+                if (lane >= d) x += y;
+            }
+            if (lane == 63) L.wsum[wave] = x;
+            lds_sync();
+            int64_t pre = carry, tot = 0;
+            for (int w = 0; w < nwaves; w++) {
+                if (w < wave) pre += L.wsum[w];
+                tot += L.wsum[w];
+            }
+            if (b < B) {
+                offs[b] = pre + x - v;
+                if (req_lds) pa.offsets[b] = pre + x - v;
+            }
+            carry += tot;
+            lds_sync();                  // wsum is rewritten by the next round
+        }
+    }
+    if (tid == 0) {
+        if (carry > total_len) L.ok = 0;
+        pa.hdr->ok = L.ok;
+        if (!L.ok && pa.dev_status) atomicOr(pa.dev_status, (int32_t)KDT_DEV_CACHE_LEN);
+    }
+    if (req_lds) lds_sync(); else __syncthreads();
+    const int ok = L.ok;
     // Groups: bt row tiles x bs splits of one request, (request, row-tile block, split block)
-    // with the split block fastest.  Work = the keys of its splits (the row tiles all cost the
-    // same); -1 = no such split anywhere in the block (or rejected lengths).
+    // with the split block fastest.  A group's work is the keys of its splits (its row tiles
+    // all cost the same).  With G <= kMaxSortGroups groups are ranked by a unique 32-bit key:
+    // bit 31 = the group has a split (a request's lengths may leave a split block empty, and
+    // rejected lengths leave every group empty), bits 30..11 = its 64-key tiles (saturated),
+    // bits 10..0 = 2047 - g (ties by index).  Larger keys go first.
     const int GR = (RT + bt - 1) / bt, GS = (S + bs - 1) / bs;
-    const int64_t G = (int64_t)B * GR * GS;
+    const int G = B * GR * GS;
     const int per = bt * bs;
-    int64_t *work = G <= kMaxSortGroups ? s_work : gwork;
-    for (int64_t g = tid; g < G; g += nth) {
-        const int b = (int)(g / ((int64_t)GR * GS)), gs = (int)(g % GS);
-        const int L = lens[b];
+    const bool grp_lds = G <= kMaxSortGroups;
+    uint32_t *key = L.key;
+    int32_t *order = grp_lds ? L.order : pa.gorder;
+    for (int g = tid; g < G; g += nth) {
+        const uint32_t q = fdiv((uint32_t)g, pa.fd_gs);
+        const int b = (int)fdiv((uint32_t)g, pa.fd_grgs), gs = g - (int)q * GS;
+        const int len = lens[b];
         int64_t w = -1;
         if (ok) {
-            const int sbr = splits_of(L, chunk, S);
+            const int sbr = req_lds ? L.sb[b] : splits(len);
             for (int sp = gs * bs; sp < gs * bs + bs && sp < sbr; sp++) {
-                const int64_t left = (int64_t)L - sp * chunk;
+                const int64_t left = (int64_t)len - (int64_t)sp * chunk;
                 w = (w < 0 ? 0 : w) + (left < chunk ? (left > 0 ? left : 0) : chunk) + (sp == 0 ? N : 0);
             }
         }
-        work[g] = w;
-    }
-    for (int64_t u = tid; u < U; u += nth) units[u] = Unit{-1, 0, 0, 0, 0, 0, 0};
-    __syncthreads();
-    for (int64_t g = tid; g < G; g += nth) {
-        int64_t rank = g;
-        if (G <= kMaxSortGroups) {      // more work first, ties by index
-            const int64_t w = work[g];
-            rank = 0;
-            for (int64_t h = 0; h < G; h++) {
-                const int64_t wh = work[h];
-                rank += (wh > w) || (wh == w && h < g);
-            }
+        if (grp_lds) {
+            const int64_t tiles = w < 0 ? 0 : (w + kKeysPerTile - 1) / kKeysPerTile;
+            key[g] = (w < 0 ? 0u : 0x80000000u) | ((uint32_t)(tiles < 0xfffff ? tiles : 0xfffff) << 11) |
+                     (uint32_t)(2047 - g);
+        } else {
+            pa.gwork[g] = w;
         }
-        gorder[rank] = (int32_t)g;
     }
-    __syncthreads();
+    if (grp_lds)                         // pad to whole 4-key reads: key 0 ranks below any group
+        for (int g = G + tid; g < ((G + 3) & ~3); g += nth) key[g] = 0u;
+    for (int u = tid; u < U; u += nth) pa.units[u] = Unit{-1, 0, 0, 0, 0, 0, 0};
+    if (grp_lds) lds_sync(); else __syncthreads();
+    if (grp_lds) {
+        // rank = #{h : key[h] > key[g]}: every thread reads the same keys (LDS broadcasts), four
+        // per read, eight reads in flight
+        const int G4 = (G + 3) >> 2;
+        const uint4 *key4 = (const uint4 *)key;
+        for (int g = tid; g < G; g += nth) {
+            const uint32_t kg = key[g];
+            int rank = 0;
+            int h = 0;
+            for (; h + 8 <= G4; h += 8) {
+                uint4 v[8];
+#pragma unroll
+                for (int k = 0; k < 8; k++) v[k] = key4[h + k];
+#pragma unroll
+                for (int k = 0; k < 8; k++) rank += (v[k].x > kg) + (v[k].y > kg) + (v[k].z > kg) + (v[k].w > kg);
+            }
+            for (; h < G4; h++) {
+                const uint4 v = key4[h];
+                rank += (v.x > kg) + (v.y > kg) + (v.z > kg) + (v.w > kg);
+            }
+            order[rank] = g;
+        }
+        lds_sync();
+    } else {
+        for (int g = tid; g < G; g += nth) order[g] = g;
+        __syncthreads();
+    }
     // Group p (in work order) goes to XCD lane x in snake order over rounds of 8 groups; its
     // unit i takes grid slot x + 8 * (round * per + i).  Slots are dealt to the XCDs
     // round-robin, so a group runs on one XCD.
-    for (int64_t e = tid; e < G * per; e += nth) {
-        const int64_t p = e / per;
-        const int i = (int)(e % per);
-        const int g = gorder[p];
-        if (work[g] < 0) continue;
-        const int b = (int)(g / ((int64_t)GR * GS));
-        const int gr = (int)((g / GS) % GR), gs = (int)(g % GS);
-        const int rt = gr * bt + i / bs, sp = gs * bs + i % bs;
-        const int sb = splits_of(lens[b], chunk, S);
+    for (int e = tid; e < G * per; e += nth) {
+        const int p = (int)fdiv((uint32_t)e, pa.fd_per);
+        const int i = e - p * per;
+        const int g = order[p];
+        if (grp_lds ? !(key[g] >> 31) : pa.gwork[g] < 0) continue;
+        const uint32_t q = fdiv((uint32_t)g, pa.fd_gs);
+        const int b = (int)fdiv((uint32_t)g, pa.fd_grgs);
+        const int gs = g - (int)q * GS, gr = (int)q - (int)fdiv(q, pa.fd_gr) * GR;
+        const int ib = (int)fdiv((uint32_t)i, pa.fd_bs);
+        const int rt = gr * bt + ib, sp = gs * bs + (i - ib * bs);
+        const int len = lens[b];
+        const int sb = req_lds ? L.sb[b] : splits(len);
         if (rt >= RT || sp >= sb) continue;
-        const int64_t round = p / kXcds;
-        const int j = (int)(p % kXcds);
+        const int round = p >> 3;        // kXcds = 8
+        const int j = p & 7;
         const int x = (round & 1) ? kXcds - 1 - j : j;
         const int64_t k0 = (int64_t)sp * chunk;
-        const int64_t k1 = k0 + chunk < (int64_t)lens[b] ? k0 + chunk : (int64_t)lens[b];
-        units[x + kXcds * (round * per + i)] = Unit{b, rt, sp, sb, (int32_t)k0, (int32_t)k1, offsets[b] + k0};
+        const int64_t k1 = k0 + chunk < (int64_t)len ? k0 + chunk : (int64_t)len;
+        pa.units[x + kXcds * (round * per + i)] = Unit{b, rt, sp, sb, (int32_t)k0, (int32_t)k1, offs[b] + k0};
     }
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs pa) {
-    __shared__ int s_ok;
-    __shared__ int64_t s_work[kMaxSortGroups];
-    plan_body(pa, &s_ok, s_work);
+    __shared__ PlanLds lds;
+    plan_body(pa, lds);
 }
 
 // Masks and plan in one launch (they are independent): workgroups 0 .. B-1 build the masks
@@ -193,12 +306,11 @@ template <int W>
 __global__ __launch_bounds__(256) void prepare_kernel(const int32_t *__restrict__ parents,
                                                       uint64_t *__restrict__ masks, PlanArgs pa) {
     __shared__ int32_t par[kMaxNodes];
-    __shared__ int s_ok;
-    __shared__ int64_t s_work[kMaxSortGroups];
+    __shared__ PlanLds lds;
     if ((int)blockIdx.x < pa.B)
         visibility_rows<W>(parents, pa.N, masks, pa.dev_status, blockIdx.x, par);
     else
-        plan_body(pa, &s_ok, s_work);
+        plan_body(pa, lds);
 }
 
 // ------------------------------------------------------------------------------ attention
@@ -997,18 +1109,22 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
 // requests.  A tile is (request, 32-row group, 32-column tile).  Lane l holds row l % 32 and
 // columns 4*(l/32) + 8g .. +3 of the tile (g = 0..3) -- the attention wave's register order,
 // so each partial load (4 packed values per lane) is 768 bytes contiguous.  Splits are merged with a running max, U of them in
-// flight.  With WS = 1 each wave of a workgroup takes its own tile; with WS = 4 (many splits)
-// the four waves share one tile, wave w taking splits w, w+4, ..., and their results are
-// merged in LDS.
+// flight.  With WS = 1 each wave of a workgroup takes its own tile; with WS = 2 or 4 (more
+// splits) WS waves share one tile, wave w of them taking splits w, w+WS, ..., and their
+// results are merged in LDS: more waves, fewer loads each, for the same bytes.
 template <int DC, int WS>
-__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kernel(AttnArgs a) {
     constexpr int NT16 = DC / 32;
-    __shared__ float s_m[WS][64], s_den[WS][64], s_acc[WS][16][64];
+    constexpr int NW = WS > kWaves ? WS : kWaves;     // waves per workgroup
+    static_assert(NW % WS == 0 && NT16 % (NW / WS) == 0 || WS == 1, "tiles of a workgroup share a row group");
+    __shared__ float s_m[NW][64], s_den[NW][64], s_acc[NW][16][64];
     const int lane = threadIdx.x & 63, half = lane >> 5;
     const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wv = WS == 1 ? 0 : wave_id;             // position among the waves sharing the tile
+    const int wv = wave_id % WS;                      // position among the waves sharing the tile
     const int64_t groups = (a.R + kRowsPerWave - 1) / kRowsPerWave;     // 32-row groups per request
-    const int64_t tile = WS == 1 ? (int64_t)blockIdx.x * kWaves + wave_id : (int64_t)blockIdx.x;
+    // a workgroup's kWaves / WS tiles are consecutive column tiles of one row group, so with
+    // WS > 1 the exits below are uniform over the workgroup (no wave skips the barrier)
+    const int64_t tile = (int64_t)blockIdx.x * (NW / WS) + wave_id / WS;
     if (tile >= (int64_t)a.B * groups * NT16) return;
     const int t16 = (int)(tile % NT16);
     const int64_t grp = (tile / NT16) % groups;
@@ -1065,21 +1181,21 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; j++) o[4 * g + j] = acc[g][j];
     if constexpr (WS > 1) {
-        s_m[wv][lane] = M;
-        s_den[wv][lane] = den;
+        s_m[wave_id][lane] = M;
+        s_den[wave_id][lane] = den;
 #pragma unroll
-        for (int k = 0; k < 16; k++) s_acc[wv][k][lane] = o[k];
+        for (int k = 0; k < 16; k++) s_acc[wave_id][k][lane] = o[k];
         __syncthreads();
         if (wv != 0) return;
         float Mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < WS; w++) Mx = fmaxf(Mx, s_m[w][lane]);
+        for (int w = wave_id; w < wave_id + WS; w++) Mx = fmaxf(Mx, s_m[w][lane]);
         tot = 0.f;
 #pragma unroll
         for (int k = 0; k < 16; k++) o[k] = 0.f;
         if (Mx != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < WS; w++) {
+            for (int w = wave_id; w < wave_id + WS; w++) {
                 const float mw = s_m[w][lane];
                 const float c = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
                 tot += c * s_den[w][lane];
@@ -1119,6 +1235,13 @@ static PlanArgs plan_args(const int32_t *cache_lens, const kdt_verify_desc &d, c
     pa.gorder = (int32_t *)(w + g.off_gorder);
     pa.units = (Unit *)(w + g.off_units);
     pa.dev_status = dev_status;
+    const int GR = (g.row_tiles + g.bt - 1) / g.bt, GS = (g.nsplit + g.bs - 1) / g.bs;
+    pa.fd_chunk = make_fastdiv((uint32_t)g.chunk);
+    pa.fd_per = make_fastdiv((uint32_t)(g.bt * g.bs));
+    pa.fd_grgs = make_fastdiv((uint32_t)GR * (uint32_t)GS);
+    pa.fd_gs = make_fastdiv((uint32_t)GS);
+    pa.fd_gr = make_fastdiv((uint32_t)GR);
+    pa.fd_bs = make_fastdiv((uint32_t)g.bs);
     return pa;
 }
 
@@ -1157,15 +1280,28 @@ hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype,
 
 hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st) {
     const int64_t tiles = (int64_t)a.B * ((a.R + kRowsPerWave - 1) / kRowsPerWave) * (d_latent / 32);
-    // many splits: four waves share a tile; otherwise one wave per tile
-    const bool share = a.S >= 16;
-    const unsigned grid = (unsigned)(share ? tiles : (tiles + kWaves - 1) / kWaves);
+    // Waves per tile: more waves share a tile while the grid stays within about 8 waves per
+    // CU (2048 on 256 CUs) and each wave keeps at least 4 splits (measured best on the
+    // split counts 8, 16, 32 and 128: 1, 4, 4 and 8 waves per tile).
+    int ws = 1;
+    while (ws < 8 && tiles * ws * 2 <= 2048 && ws * 2 * 4 <= a.S) ws *= 2;
+    const int nw = ws > kWaves ? ws : kWaves;
+    const int64_t tpb = nw / ws;
+    const unsigned grid = (unsigned)((tiles + tpb - 1) / tpb);
+    const unsigned block = (unsigned)(64 * nw);
+    auto go = [&](auto dc) {
+        constexpr int DCv = decltype(dc)::value;
+        switch (ws) {
+            case 8: combine_kernel<DCv, 8><<<grid, block, 0, st>>>(a); break;
+            case 4: combine_kernel<DCv, 4><<<grid, block, 0, st>>>(a); break;
+            case 2: combine_kernel<DCv, 2><<<grid, block, 0, st>>>(a); break;
+            default: combine_kernel<DCv, 1><<<grid, block, 0, st>>>(a); break;
+        }
+    };
     if (d_latent == 512) {
-        if (share) combine_kernel<512, 4><<<grid, 256, 0, st>>>(a);
-        else combine_kernel<512, 1><<<grid, 256, 0, st>>>(a);
+        go(std::integral_constant<int, 512>{});
     } else if (d_latent == 64) {
-        if (share) combine_kernel<64, 4><<<grid, 256, 0, st>>>(a);
-        else combine_kernel<64, 1><<<grid, 256, 0, st>>>(a);
+        go(std::integral_constant<int, 64>{});
     } else {
         return hipErrorInvalidValue;
     }
