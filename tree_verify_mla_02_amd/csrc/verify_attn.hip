@@ -1112,23 +1112,25 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
 // flight.  With WS = 1 each wave of a workgroup takes its own tile; with WS = 2 or 4 (more
 // splits) WS waves share one tile, wave w of them taking splits w, w+WS, ..., and their
 // results are merged in LDS: more waves, fewer loads each, for the same bytes.
-template <int DC, int WS>
+template <int DC, int WS, int GC>
 __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kernel(AttnArgs a) {
     constexpr int NT16 = DC / 32;
+    constexpr int NSUB = 4 / GC;                      // waves over one tile's 4 column groups
     constexpr int NW = WS > kWaves ? WS : kWaves;     // waves per workgroup
-    static_assert(NW % WS == 0 && NT16 % (NW / WS) == 0 || WS == 1, "tiles of a workgroup share a row group");
-    __shared__ float s_m[NW][64], s_den[NW][64], s_acc[NW][16][64];
+    static_assert(NW % WS == 0 && (NT16 * NSUB) % (NW / WS) == 0 || WS == 1, "tiles of a workgroup share a row group");
+    __shared__ float s_m[NW][64], s_den[NW][64], s_acc[NW][4 * GC][64];
     const int lane = threadIdx.x & 63, half = lane >> 5;
     const int wave_id = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wv = wave_id % WS;                      // position among the waves sharing the tile
     const int64_t groups = (a.R + kRowsPerWave - 1) / kRowsPerWave;     // 32-row groups per request
-    // a workgroup's kWaves / WS tiles are consecutive column tiles of one row group, so with
+    // a workgroup's NW / WS (sub-)tiles are consecutive column tiles of one row group, so with
     // WS > 1 the exits below are uniform over the workgroup (no wave skips the barrier)
     const int64_t tile = (int64_t)blockIdx.x * (NW / WS) + wave_id / WS;
-    if (tile >= (int64_t)a.B * groups * NT16) return;
-    const int t16 = (int)(tile % NT16);
-    const int64_t grp = (tile / NT16) % groups;
-    const int b = (int)(tile / (NT16 * groups));
+    if (tile >= (int64_t)a.B * groups * NT16 * NSUB) return;
+    const int sub = (int)(tile % NSUB);
+    const int t16 = (int)((tile / NSUB) % NT16);
+    const int64_t grp = (tile / (NSUB * NT16)) % groups;
+    const int b = (int)(tile / (NSUB * NT16 * groups));
     const int ok = a.hdr->ok;                         // both loads in flight together
     const int sb = splits_of(a.lens[b], a.chunk, a.S);
     if (!ok || sb <= 1) return;                       // uniform over the workgroup
@@ -1136,16 +1138,16 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
     const bool valid = r < a.R;
     const int64_t rc = valid ? r : a.R - 1;
     const int rt = (int)(grp / kWaves), wave = (int)(grp % kWaves);
-    float acc[4][4];
+    float acc[GC][4];
 #pragma unroll
-    for (int g = 0; g < 4; g++)
+    for (int g = 0; g < GC; g++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[g][j] = 0.f;
     float M = -INFINITY, den = 0.f;
     constexpr int U = 8;                              // splits in flight per wave
     for (int s0 = wv; s0 < sb; s0 += U * WS) {
         float2 ml[U];
-        float4 x[U][4];
+        float4 x[U][GC];
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int sp = s0 + u * WS;
@@ -1154,7 +1156,7 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
                 const int64_t blk = (((int64_t)b * a.S + sp) * a.RT + rt) * kWaves + wave;
                 const uint32_t *src = a.part_o + blk * (kRowsPerWave * DC / 4 * 3) + lane * 3;
 #pragma unroll
-                for (int g = 0; g < 4; g++) x[u][g] = unpack24x4(src + (t16 * 4 + g) * 192);
+                for (int g = 0; g < GC; g++) x[u][g] = unpack24x4(src + (t16 * 4 + sub * GC + g) * 192);
             }
         }
 #pragma unroll
@@ -1165,7 +1167,7 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
                 const float w = __builtin_amdgcn_exp2f(ml[u].x - mn);
                 den = den * c + w * ml[u].y;
 #pragma unroll
-                for (int g = 0; g < 4; g++) {
+                for (int g = 0; g < GC; g++) {
                     acc[g][0] = acc[g][0] * c + w * x[u][g].x;
                     acc[g][1] = acc[g][1] * c + w * x[u][g].y;
                     acc[g][2] = acc[g][2] * c + w * x[u][g].z;
@@ -1175,16 +1177,16 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
             }
         }
     }
-    float tot = den, o[16];
+    float tot = den, o[4 * GC];
 #pragma unroll
-    for (int g = 0; g < 4; g++)
+    for (int g = 0; g < GC; g++)
 #pragma unroll
         for (int j = 0; j < 4; j++) o[4 * g + j] = acc[g][j];
     if constexpr (WS > 1) {
         s_m[wave_id][lane] = M;
         s_den[wave_id][lane] = den;
 #pragma unroll
-        for (int k = 0; k < 16; k++) s_acc[wave_id][k][lane] = o[k];
+        for (int k = 0; k < 4 * GC; k++) s_acc[wave_id][k][lane] = o[k];
         __syncthreads();
         if (wv != 0) return;
         float Mx = -INFINITY;
@@ -1192,7 +1194,7 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
         for (int w = wave_id; w < wave_id + WS; w++) Mx = fmaxf(Mx, s_m[w][lane]);
         tot = 0.f;
 #pragma unroll
-        for (int k = 0; k < 16; k++) o[k] = 0.f;
+        for (int k = 0; k < 4 * GC; k++) o[k] = 0.f;
         if (Mx != -INFINITY) {
 #pragma unroll
             for (int w = wave_id; w < wave_id + WS; w++) {
@@ -1200,7 +1202,7 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
                 const float c = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - Mx);
                 tot += c * s_den[w][lane];
 #pragma unroll
-                for (int k = 0; k < 16; k++) o[k] += c * s_acc[w][k][lane];
+                for (int k = 0; k < 4 * GC; k++) o[k] += c * s_acc[w][k][lane];
             }
         }
     }
@@ -1208,8 +1210,9 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
     float *dst = a.out + ((int64_t)b * a.R + r) * DC + t16 * 32 + 4 * half;
 #pragma unroll
-    for (int g = 0; g < 4; g++)
-        *(float4 *)(dst + 8 * g) = make_float4(o[4 * g] * inv, o[4 * g + 1] * inv, o[4 * g + 2] * inv, o[4 * g + 3] * inv);
+    for (int g = 0; g < GC; g++)
+        *(float4 *)(dst + 8 * (sub * GC + g)) =
+            make_float4(o[4 * g] * inv, o[4 * g + 1] * inv, o[4 * g + 2] * inv, o[4 * g + 3] * inv);
 }
 
 // ------------------------------------------------------------------------------ launchers
@@ -1280,28 +1283,36 @@ hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype,
 
 hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st) {
     const int64_t tiles = (int64_t)a.B * ((a.R + kRowsPerWave - 1) / kRowsPerWave) * (d_latent / 32);
-    // Waves per tile: more waves share a tile while the grid stays within about 8 waves per
-    // CU (2048 on 256 CUs) and each wave keeps at least 4 splits (measured best on the
-    // split counts 8, 16, 32 and 128: 1, 4, 4 and 8 waves per tile).
-    int ws = 1;
+    // Waves per tile: first more waves share a tile (each keeping at least 4 splits), then a
+    // tile's four column groups go to 2 or 4 waves, while the grid stays within about 8 waves
+    // per CU (2048 on 256 CUs).  Measured best on the split counts 8, 16, 32 and 128 (the
+    // Kimi, 7-node, 16-node and decode shapes): 1 x 4, 4 x 2, 4 x 4 and 8 x 1 waves x groups.
+    int ws = 1, gc = 4;
     while (ws < 8 && tiles * ws * 2 <= 2048 && ws * 2 * 4 <= a.S) ws *= 2;
+    while (gc > 1 && tiles * ws * (4 / gc) * 2 <= 2048) gc /= 2;
+    const int64_t subs = tiles * (4 / gc);
     const int nw = ws > kWaves ? ws : kWaves;
     const int64_t tpb = nw / ws;
-    const unsigned grid = (unsigned)((tiles + tpb - 1) / tpb);
+    const unsigned grid = (unsigned)((subs + tpb - 1) / tpb);
     const unsigned block = (unsigned)(64 * nw);
-    auto go = [&](auto dc) {
-        constexpr int DCv = decltype(dc)::value;
+    auto go = [&](auto dc, auto gcv) {
+        constexpr int DCv = decltype(dc)::value, GC = decltype(gcv)::value;
         switch (ws) {
-            case 8: combine_kernel<DCv, 8><<<grid, block, 0, st>>>(a); break;
-            case 4: combine_kernel<DCv, 4><<<grid, block, 0, st>>>(a); break;
-            case 2: combine_kernel<DCv, 2><<<grid, block, 0, st>>>(a); break;
-            default: combine_kernel<DCv, 1><<<grid, block, 0, st>>>(a); break;
+            case 8: combine_kernel<DCv, 8, GC><<<grid, block, 0, st>>>(a); break;
+            case 4: combine_kernel<DCv, 4, GC><<<grid, block, 0, st>>>(a); break;
+            case 2: combine_kernel<DCv, 2, GC><<<grid, block, 0, st>>>(a); break;
+            default: combine_kernel<DCv, 1, GC><<<grid, block, 0, st>>>(a); break;
         }
     };
+    auto go_dc = [&](auto dc) {
+        if (gc == 4) go(dc, std::integral_constant<int, 4>{});
+        else if (gc == 2) go(dc, std::integral_constant<int, 2>{});
+        else go(dc, std::integral_constant<int, 1>{});
+    };
     if (d_latent == 512) {
-        go(std::integral_constant<int, 512>{});
+        go_dc(std::integral_constant<int, 512>{});
     } else if (d_latent == 64) {
-        go(std::integral_constant<int, 64>{});
+        go_dc(std::integral_constant<int, 64>{});
     } else {
         return hipErrorInvalidValue;
     }
