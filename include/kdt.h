@@ -63,7 +63,8 @@ typedef enum {
 enum {
     KDT_DEV_OK = 0,
     KDT_DEV_BAD_PARENT = 1,    /* some parent[b,j] on a walked path is outside [-1, j-1] */
-    KDT_DEV_CACHE_LEN = 2      /* some cache_lens[b] < 0 or > max_cache_len, or their sum > total_cache_len */
+    KDT_DEV_CACHE_LEN = 2,     /* some cache_lens[b] < 0 or > max_cache_len, or their sum > total_cache_len */
+    KDT_DEV_BAD_ACCEPT = 4     /* kdt_kv_compact: a length or path entry out of range, or too many rows */
 };
 
 /* Element type of q_lat, q_rope and the cache / tree rows; `out` is always fp32. */
@@ -163,6 +164,55 @@ int kdt_tree_verify_combine(float *out, const kdt_verify_desc *desc, void *works
 int kdt_tree_verify_prepare(const int32_t *parents, uint64_t *bitmask, const int32_t *cache_lens,
                             const kdt_verify_desc *desc, void *workspace, size_t workspace_bytes,
                             int32_t *dev_status, void *stream);
+
+/*
+ * kdt_tree_accept -- greedy acceptance closing a verify pass.  Accepted tokens are committed
+ * and rejected ones discarded, and the target's prediction at the final accepted node is the
+ * bonus token ("The Capstone Validation", sections "Context and Motivation" and "What the
+ * Test Actually Validated"); the engine runs a greedy tree-accept kernel ("Validating the
+ * Native Engine", section "The Broader Context").
+ *   parents     [B, N] int32, device: parent < child, -1 at depth 1 (as kdt_build_visibility).
+ *   tokens      [B, N] int32, device: each node's drafted token id.
+ *   target_next [B, N] int32, device: the target's greedy token at each node's position.
+ *   root_next   [B] int32, device: the target's greedy token after the committed context.
+ *   path        [B, N] int32, device, out: accepted node ids in root-to-leaf order, then -1.
+ *   accept_len  [B] int32, device, out: number of accepted nodes.
+ *   bonus       [B] int32, device, out: the target's token after the last accepted node
+ *               (root_next when none is accepted).
+ * A node is accepted when its parent is (the committed context at depth 1) and its token is
+ * the target's greedy token at the parent's position.  Among children with equal tokens the
+ * lowest index is taken; children are looked for only above the parent's index, so a
+ * malformed parent array ends the walk rather than looping.  N must lie in [1, 256].
+ */
+int kdt_tree_accept(const int32_t *parents, const int32_t *tokens, const int32_t *target_next,
+                    const int32_t *root_next, int32_t batch, int32_t num_nodes, int32_t *path,
+                    int32_t *accept_len, int32_t *bonus, void *stream);
+
+/*
+ * kdt_kv_compact -- post-verify compaction of the committed cache ("Validating the Native
+ * Engine", section "The Broader Context": a KV cache with post-verify compaction): each
+ * request's accepted tree rows are committed right after its committed rows.
+ *   ckv_cache, krope_cache, cache_lens: the packed cache exactly as for kdt_tree_verify_attn
+ *               (desc gives batch, num_nodes, d_latent, d_rope, dtype, the row strides,
+ *               max_cache_len and total_cache_len).
+ *   tree_ckv, tree_krope [B, N, d_c], [B, N, d_r] at desc's tree strides.
+ *   path, accept_len: as written by kdt_tree_accept.
+ *   ckv_out, krope_out: destination rows at the source's strides, room for out_capacity_rows
+ *               rows.  Request b's new rows start at the sum of the earlier new lengths: its
+ *               committed rows, then its accepted rows in path order.
+ *   new_lens    [B] int32, device, out: cache_lens + accept_len.
+ * The destination must not overlap an input, except in place (ckv_out == ckv_cache and
+ * krope_out == krope_cache) with batch 1, where the committed rows stay and only the
+ * accepted rows are written.  Device-side checks: a length outside [0, max_cache_len], an
+ * accept_len outside [0, N], more than total_cache_len source rows or more than
+ * out_capacity_rows destination rows writes nothing; a path entry that names no node leaves
+ * that request (rows and new length) unwritten; both OR KDT_DEV_BAD_ACCEPT into *dev_status.
+ */
+int kdt_kv_compact(const void *ckv_cache, const void *krope_cache, const int32_t *cache_lens,
+                   const void *tree_ckv, const void *tree_krope, const int32_t *path,
+                   const int32_t *accept_len, void *ckv_out, void *krope_out, int32_t *new_lens,
+                   int64_t out_capacity_rows, const kdt_verify_desc *desc, int32_t *dev_status,
+                   void *stream);
 
 /* Number of key splits per request the plan uses for desc on the current device (1 = no
  * split), or -1 for an invalid desc. */

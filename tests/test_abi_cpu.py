@@ -87,3 +87,43 @@ def test_desc_validation_on_host(field, value, code):
     assert lib.kdt_last_status() == code
     assert lib.kdt_tree_verify_attn(*([None] * 8), ctypes.c_float(1.0), None, ctypes.byref(d), None, 0, None,
                                     None) == code
+
+
+def test_tree_accept_rejects_bad_arguments_on_host():
+    lib = kdt.load()
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: every call fails before any launch
+    args = [fake] * 4 + [1, 8] + [fake] * 3 + [None]   # valid as given (never launched here)
+    bad = list(args)
+    bad[1] = None
+    assert lib.kdt_tree_accept(*bad) == _lib.KDT_ERR_INVALID_ARG
+    bad = list(args)
+    bad[5] = 257
+    assert lib.kdt_tree_accept(*bad) == _lib.KDT_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[4] = 0
+    assert lib.kdt_tree_accept(*bad) == _lib.KDT_ERR_INVALID_ARG
+    bad = list(args)
+    bad[6] = ctypes.c_void_p((1 << 20) + 2)
+    assert lib.kdt_tree_accept(*bad) == _lib.KDT_ERR_MISALIGNED
+
+
+def test_kv_compact_rejects_bad_arguments_on_host():
+    lib = kdt.load()
+    d = _lib.VerifyDesc(batch=2, num_nodes=8, num_heads=4, d_latent=512, d_rope=64, dtype=_lib.KDT_BF16,
+                        max_cache_len=16, total_cache_len=32, q_lat_stride=512, q_rope_stride=64, ckv_stride=576,
+                        krope_stride=576, tree_ckv_stride=576, tree_krope_stride=576)
+    a, b2 = ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21)   # never dereferenced
+
+    def call(ckv=a, krope=a, lens=a, tc=a, tr=a, path=a, acc=a, oc=b2, orope=b2, nl=a, cap=64, desc=d):
+        return lib.kdt_kv_compact(ckv, krope, lens, tc, tr, path, acc, oc, orope, nl, cap, ctypes.byref(desc),
+                                  None, None)
+    assert call(lens=None) == _lib.KDT_ERR_INVALID_ARG
+    assert call(nl=None) == _lib.KDT_ERR_INVALID_ARG
+    assert call(cap=-1) == _lib.KDT_ERR_INVALID_ARG
+    assert call(tc=ctypes.c_void_p((1 << 20) + 8)) == _lib.KDT_ERR_MISALIGNED
+    assert call(acc=ctypes.c_void_p((1 << 20) + 2)) == _lib.KDT_ERR_MISALIGNED
+    assert call(oc=a, orope=b2) == _lib.KDT_ERR_INVALID_ARG          # in place for one part only
+    assert call(oc=a, orope=a) == _lib.KDT_ERR_INVALID_ARG           # in place with batch 2
+    assert b"batch 1" in lib.kdt_last_error()
+    d.num_nodes = 300
+    assert call() == _lib.KDT_ERR_UNSUPPORTED

@@ -16,13 +16,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkdt.so")
 
 KDT_OK, KDT_ERR_INVALID_ARG, KDT_ERR_UNSUPPORTED, KDT_ERR_MISALIGNED, KDT_ERR_WORKSPACE, KDT_ERR_HIP = range(6)
-KDT_DEV_BAD_PARENT, KDT_DEV_CACHE_LEN = 1, 2
+KDT_DEV_BAD_PARENT, KDT_DEV_CACHE_LEN, KDT_DEV_BAD_ACCEPT = 1, 2, 4
 KDT_BF16, KDT_F32 = 0, 1
 
 EXPORTS = [
     "kdt_build_visibility", "kdt_tree_verify_workspace_size", "kdt_tree_verify_attn",
     "kdt_tree_verify_plan", "kdt_tree_verify_prepare", "kdt_tree_verify_attend", "kdt_tree_verify_combine",
     "kdt_tree_verify_num_splits", "kdt_status_string", "kdt_last_error", "kdt_last_status", "kdt_version",
+    "kdt_tree_accept", "kdt_kv_compact",
 ]
 
 
@@ -65,6 +66,8 @@ def load() -> ctypes.CDLL:
     lib.kdt_tree_verify_prepare.argtypes = [vp, vp, vp, dp, vp, sz, vp, vp]
     lib.kdt_tree_verify_attend.argtypes = [vp] * 7 + [ctypes.c_float, vp, dp, vp, sz, vp]
     lib.kdt_tree_verify_combine.argtypes = [vp, dp, vp, sz, vp]
+    lib.kdt_tree_accept.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
+    lib.kdt_kv_compact.argtypes = [vp] * 10 + [i64, dp, vp, vp]
     lib.kdt_status_string.restype = ctypes.c_char_p
     lib.kdt_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -221,3 +224,44 @@ def attend(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, bitmask, scale, out,
 def combine(out, desc: VerifyDesc, workspace, stream=None):
     _check(load().kdt_tree_verify_combine(_ptr(out), ctypes.byref(desc), _ptr(workspace), workspace.numel(),
                                           _stream(stream)))
+
+
+def _int32_2d(t, name):
+    if t.dtype != torch.int32 or not t.is_contiguous() or t.dim() != 2:
+        raise ValueError(f"{name} must be a contiguous [B, N] int32 tensor")
+
+
+def tree_accept(parents, tokens, target_next, root_next, path=None, accept_len=None, bonus=None, stream=None):
+    """Greedy acceptance: (path [B, N], accept_len [B], bonus [B]), int32 on the device."""
+    for t, n in ((parents, "parents"), (tokens, "tokens"), (target_next, "target_next")):
+        _int32_2d(t, n)
+    B, N = parents.shape
+    if tokens.shape != (B, N) or target_next.shape != (B, N):
+        raise ValueError("parents, tokens and target_next must have the same [B, N] shape")
+    if root_next.dtype != torch.int32 or root_next.shape != (B,) or not root_next.is_contiguous():
+        raise ValueError("root_next must be a contiguous [B] int32 tensor")
+    dev = parents.device
+    if path is None:
+        path = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(load().kdt_tree_accept(_ptr(parents), _ptr(tokens), _ptr(target_next), _ptr(root_next), B, N,
+                                  _ptr(path), _ptr(accept_len), _ptr(bonus), _stream(stream)))
+    return path, accept_len, bonus
+
+
+def kv_compact(ckv, krope, cache_lens, tree_ckv, tree_krope, path, accept_len, desc: VerifyDesc, ckv_out,
+               krope_out, new_lens=None, capacity_rows: Optional[int] = None, dev_status=None, stream=None):
+    """Commit the accepted tree rows after each request's committed rows (into ckv_out /
+    krope_out, same row strides as the source); returns new_lens [B] int32."""
+    if new_lens is None:
+        new_lens = torch.empty(desc.batch, dtype=torch.int32, device=cache_lens.device)
+    if capacity_rows is None:
+        es = ckv_out.element_size()
+        capacity_rows = (ckv_out.untyped_storage().nbytes() - ckv_out.storage_offset() * es) // (desc.ckv_stride * es)
+    _check(load().kdt_kv_compact(_ptr(ckv), _ptr(krope), _ptr(cache_lens), _ptr(tree_ckv), _ptr(tree_krope),
+                                 _ptr(path), _ptr(accept_len), _ptr(ckv_out), _ptr(krope_out), _ptr(new_lens),
+                                 int(capacity_rows), ctypes.byref(desc), _ptr(dev_status), _stream(stream)))
+    return new_lens

@@ -246,6 +246,54 @@ int kdt_build_visibility(const int32_t *parents, int32_t batch, int32_t num_node
     return ok();
 }
 
+int kdt_tree_accept(const int32_t *parents, const int32_t *tokens, const int32_t *target_next,
+                    const int32_t *root_next, int32_t batch, int32_t num_nodes, int32_t *path, int32_t *accept_len,
+                    int32_t *bonus, void *stream) {
+    if (!parents || !tokens || !target_next || !root_next || !path || !accept_len || !bonus)
+        return fail(KDT_ERR_INVALID_ARG, "no pointer of kdt_tree_accept may be NULL");
+    if (batch < 1) return fail(KDT_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (num_nodes < 1 || num_nodes > kdt::kMaxNodes)
+        return fail(KDT_ERR_UNSUPPORTED, "num_nodes must be in [1, %d] (got %d)", kdt::kMaxNodes, num_nodes);
+    const void *ptrs[] = {parents, tokens, target_next, root_next, path, accept_len, bonus};
+    for (const void *q : ptrs)
+        if ((uintptr_t)q & 3u) return fail(KDT_ERR_MISALIGNED, "int32 arrays must be 4-byte aligned");
+    if (batch > INT32_MAX / 2) return fail(KDT_ERR_INVALID_ARG, "batch too large for one launch");
+    const hipError_t e = kdt::launch_accept(parents, tokens, target_next, root_next, batch, num_nodes, path,
+                                            accept_len, bonus, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "accept launch");
+    return ok();
+}
+
+int kdt_kv_compact(const void *ckv_cache, const void *krope_cache, const int32_t *cache_lens, const void *tree_ckv,
+                   const void *tree_krope, const int32_t *path, const int32_t *accept_len, void *ckv_out,
+                   void *krope_out, int32_t *new_lens, int64_t out_capacity_rows, const kdt_verify_desc *desc,
+                   int32_t *dev_status, void *stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (!ckv_cache || !krope_cache || !cache_lens || !tree_ckv || !tree_krope || !path || !accept_len ||
+        !ckv_out || !krope_out || !new_lens)
+        return fail(KDT_ERR_INVALID_ARG, "only dev_status of kdt_kv_compact may be NULL");
+    if (out_capacity_rows < 0) return fail(KDT_ERR_INVALID_ARG, "out_capacity_rows must be >= 0");
+    const void *rows[] = {ckv_cache, krope_cache, tree_ckv, tree_krope, ckv_out, krope_out};
+    for (const void *q : rows)
+        if (!aligned16(q)) return fail(KDT_ERR_MISALIGNED, "row pointers must be 16-byte aligned");
+    const void *ints[] = {cache_lens, path, accept_len, new_lens};
+    for (const void *q : ints)
+        if ((uintptr_t)q & 3u) return fail(KDT_ERR_MISALIGNED, "int32 arrays must be 4-byte aligned");
+    const bool lat_in_place = ckv_out == ckv_cache, rope_in_place = krope_out == krope_cache;
+    if (lat_in_place != rope_in_place)
+        return fail(KDT_ERR_INVALID_ARG, "compaction is in place for both parts or for neither");
+    if (lat_in_place && desc->batch != 1)
+        return fail(KDT_ERR_INVALID_ARG, "in-place compaction needs batch 1 (later requests would move)");
+    const int64_t rows_max = desc->max_cache_len + desc->num_nodes;
+    if ((rows_max + 31) / 32 > 65535) return fail(KDT_ERR_UNSUPPORTED, "max_cache_len too large for one launch");
+    const hipError_t e = kdt::launch_compact(ckv_cache, krope_cache, cache_lens, tree_ckv, tree_krope, path,
+                                             accept_len, ckv_out, krope_out, new_lens, out_capacity_rows, *desc,
+                                             dev_status, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "compaction launch");
+    return ok();
+}
+
 size_t kdt_tree_verify_workspace_size(const kdt_verify_desc *desc) {
     kdt::Geometry g;
     if (geometry_for(desc, &g)) return 0;

@@ -82,5 +82,12 @@ hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t
 hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units,
                          hipStream_t st);
 hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st);
+hipError_t launch_accept(const int32_t *parents, const int32_t *tokens, const int32_t *target_next,
+                         const int32_t *root_next, int B, int N, int32_t *path, int32_t *accept_len,
+                         int32_t *bonus, hipStream_t st);
+hipError_t launch_compact(const void *ckv, const void *krope, const int32_t *cache_lens, const void *tree_ckv,
+                          const void *tree_krope, const int32_t *path, const int32_t *accept_len, void *ckv_out,
+                          void *krope_out, int32_t *new_lens, int64_t capacity, const kdt_verify_desc &d,
+                          int32_t *dev_status, hipStream_t st);
 
 }  // namespace kdt
