@@ -261,6 +261,136 @@ def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0):
                       f"in {dt:.2f} s on {cores} threads"}
 
 
+def accept_inputs(inp, seed):
+    """Drafted tokens (distinct among siblings) and target predictions that follow a random
+    root-to-leaf walk (its first step always, each later one with probability 0.85), for the
+    workload's trees."""
+    par = inp.parents.numpy()
+    B, N = par.shape
+    rng = np.random.default_rng([seed, 77])
+    tok = rng.permutation(B * N * 4)[: B * N].reshape(B, N).astype(np.int32)
+    nxt = rng.integers(0, 1 << 20, size=(B, N)).astype(np.int32)
+    root = rng.integers(0, 1 << 20, size=B).astype(np.int32)
+    for b in range(B):
+        kids = {}
+        for j in range(N):
+            kids.setdefault(int(par[b, j]), []).append(j)
+        cur = -1
+        while kids.get(cur) and (cur < 0 or rng.random() < 0.85):
+            j = int(rng.choice(kids[cur]))
+            if cur < 0:
+                root[b] = tok[b, j]
+            else:
+                nxt[b, cur] = tok[b, j]
+            cur = j
+    return par.astype(np.int32), tok, nxt, root
+
+
+def run_next_row(args):
+    """The greedy tree-accept or the KV compaction kernel alone: K launches bracketed by
+    fence-free events, each launch on the same inputs (both kernels are idempotent)."""
+    import tree_verify_mla_02_amd as kdt
+    from oracle import accept as oracle_accept
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = workloads.make_inputs(args.workload, seed=args.seed)
+    sp = inp.spec
+    par, tok, nxt, root = accept_inputs(inp, args.seed)
+    B, N = par.shape
+    d_par, d_tok, d_nxt, d_root = (torch.from_numpy(x).to(dev) for x in (par, tok, nxt, root))
+    stream = torch.cuda.current_stream(dev)
+    path, acc, bonus = kdt.tree_accept(d_par, d_tok, d_nxt, d_root, stream=stream)
+    torch.cuda.synchronize()
+    he = HipEvents()
+    if args.row == "accept":
+        def launch():
+            kdt.tree_accept(d_par, d_tok, d_nxt, d_root, path, acc, bonus, stream=stream)
+        # bytes the walk must touch: the three [B, N] arrays and root_next, the outputs
+        nbytes = B * N * 12 + B * 4 + B * N * 4 + B * 8
+        work = B
+    else:
+        dc = sp.d_latent
+        kv, tkv = inp.kv_cache.to(dev), inp.tree_kv.to(dev)
+        lens_np = inp.cache_lens.numpy().astype(np.int64)
+        T = int(lens_np.sum())
+        acc_np = acc.cpu().numpy().astype(np.int64)
+        rows = T + int(acc_np.sum())
+        out = torch.empty((rows, kv.shape[1]), dtype=kv.dtype, device=dev)
+        q_lat = torch.empty((B, N, 1, dc), dtype=kv.dtype, device=dev)
+        q_rope = torch.empty((B, N, 1, kv.shape[1] - dc), dtype=kv.dtype, device=dev)
+        desc = kdt.make_desc(q_lat, q_rope, kv[:, :dc], kv[:, dc:], tkv[:, :, :dc], tkv[:, :, dc:],
+                             int(lens_np.max()), T)
+        d_lens = inp.cache_lens.to(dev)
+        new_lens = torch.empty(B, dtype=torch.int32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def launch():
+            kdt.kv_compact(kv[:, :dc], kv[:, dc:], d_lens, tkv[:, :, :dc], tkv[:, :, dc:], path, acc, desc,
+                           out[:, :dc], out[:, dc:], new_lens=new_lens, capacity_rows=rows, dev_status=status,
+                           stream=stream)
+        e = kv.element_size()
+        nbytes = 2 * rows * kv.shape[1] * e          # every new row read once and written once
+        work = rows
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    if args.row == "compact" and int(status.item()) != 0:
+        raise SystemExit(f"device status {int(status.item())} on the benchmark inputs")
+    evs = [(he.create(), he.create()) for _ in range(args.steps)]
+    ev0, ev1 = he.create(), he.create()
+    he.record(ev0, stream)
+    for i in range(args.steps):
+        he.record(evs[i][0], stream)
+        launch()
+        he.record(evs[i][1], stream)
+    he.record(ev1, stream)
+    torch.cuda.synchronize()
+    step_ms = he.elapsed_ms(ev0, ev1) / args.steps
+    each = np.array([he.elapsed_ms(a, b) for a, b in evs])
+    he.close()
+    k_ms = float(each.mean())
+    achieved = nbytes / (k_ms * 1e-3) / 1e9
+    line = {
+        "metric": "greedy tree-accept requests/s" if args.row == "accept" else "post-verify KV compaction GB/s",
+        "value": round(work / (step_ms * 1e-3), 3) if args.row == "accept" else round(nbytes / (step_ms * 1e-3) / 1e9, 3),
+        "unit": "requests/s" if args.row == "accept" else "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32" if args.row == "accept" else sp.dtype,
+        "data": "synthetic (seeded tokens and target predictions on the workload's draft trees)",
+        "config": {"workload": f"{args.row} on {sp.name}: B={B} requests, N={N} nodes"
+                               + (f", {int(inp.cache_lens.sum())} committed + {work - int(inp.cache_lens.sum())}"
+                                  f" accepted rows of {(sp.d_latent + sp.d_rope)} {sp.dtype}" if args.row == "compact" else ""),
+                   "batch": B, "nodes": N},
+        "kernel_ms": round(k_ms, 5),
+        "kernel_ms_p10_p50_p90": [round(float(np.percentile(each, q)), 5) for q in (10, 50, 90)],
+        "kernel_source_hash": kernel_source_hash(),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        cores = len(os.sched_getaffinity(0))
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            if args.row == "accept":
+                oracle_accept.tree_accept(par, tok, nxt, root)
+            else:
+                oracle_accept.kv_compact(inp.kv_cache[:, :dc].view(torch.int16).numpy(),
+                                         inp.kv_cache[:, dc:].view(torch.int16).numpy(), lens_np,
+                                         inp.tree_kv[:, :, :dc].view(torch.int16).numpy(),
+                                         inp.tree_kv[:, :, dc:].view(torch.int16).numpy(),
+                                         path.cpu().numpy(), acc_np)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or dt * (reps + 1) / reps > 30.0:
+                break
+        line["cpu_baseline"] = {
+            "value": round(reps * work / dt, 3) if args.row == "accept" else round(reps * nbytes / dt / 1e9, 3),
+            "unit": line["unit"], "cores": 1, "kind": "oracle",
+            "sample": f"{reps} whole launch(es) of the same inputs in {dt:.2f} s (plain Python / numpy, one thread)"}
+    return line
+
+
 # HBM traffic of the attention kernel per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # summarised under profiles/.  The summary records a hash of the kernel sources it was taken
 # on; when the sources have changed since, the figure no longer describes this kernel and
@@ -304,12 +434,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="attention launches timed after flushing L2 and MALL (0 to skip)")
+    ap.add_argument("--row", default="verify", choices=["verify", "accept", "compact"],
+                    help="verify: the tree-verify attention step (default); accept / compact: the greedy "
+                         "tree-accept or the KV compaction kernel alone, on the workload's trees and lengths")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X with no sharding "
-              "(see DESIGN.md for how it would shard); run it with --gpus 1.", file=sys.stderr)
+              "(the design notes describe how it would shard); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -319,6 +452,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_direction": n, "launches": args.steps}), flush=True)
+        return
+    if args.row != "verify":
+        print(json.dumps(run_next_row(args)), flush=True)
         return
     line, inp = run(args)
     if not args.no_cpu_baseline:
