@@ -391,6 +391,75 @@ def run_next_row(args):
     return line
 
 
+def run_tree_row(args):
+    """The best-first tree builder alone on the workload's tree shape (requests, nodes, depth,
+    top-k): K launches bracketed by fence-free events on the same drafter log probabilities."""
+    import tree_verify_mla_02_amd as kdt
+    from oracle import tree_build as oracle_tree
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sp = workloads.SPECS[args.workload]
+    B, N = sp.batch, sp.nodes
+    D, K = (sp.depth, sp.topk) if sp.tree == "bestfirst" else (8, 8)
+    rng = np.random.default_rng([args.seed, 91])
+    lp = np.stack([workloads.drafter_logprobs(rng, D, K) for _ in range(B)]).astype(np.float32)
+    cand = rng.integers(0, 160000, size=(B, D, K)).astype(np.int32)
+    d_lp, d_cand = torch.from_numpy(lp).to(dev), torch.from_numpy(cand).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    outs = kdt.build_tree(d_lp, d_cand, N, stream=stream)
+    torch.cuda.synchronize()
+    want = oracle_tree.best_first_tree(lp, cand, N)
+    for g, w in zip(outs, want):
+        if not np.array_equal(g.cpu().numpy(), w):
+            raise SystemExit("tree builder output differs from the oracle on the benchmark inputs")
+
+    def launch():
+        kdt.build_tree(d_lp, d_cand, N, *outs, stream=stream)
+    he = HipEvents()
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize()
+    evs = [(he.create(), he.create()) for _ in range(args.steps)]
+    ev0, ev1 = he.create(), he.create()
+    he.record(ev0, stream)
+    for i in range(args.steps):
+        he.record(evs[i][0], stream)
+        launch()
+        he.record(evs[i][1], stream)
+    he.record(ev1, stream)
+    torch.cuda.synchronize()
+    step_ms = he.elapsed_ms(ev0, ev1) / args.steps
+    each = np.array([he.elapsed_ms(a, b) for a, b in evs])
+    he.close()
+    k_ms = float(each.mean())
+    line = {
+        "metric": "best-first draft-tree build requests/s", "value": round(B / (step_ms * 1e-3), 3),
+        "unit": "requests/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic (seeded drafter log probabilities, logits N(0, 2^2), sorted per depth)",
+        "config": {"workload": f"tree on {sp.name}: B={B} requests, N={N} nodes, depth<={D}, top-{K}",
+                   "batch": B, "nodes": N, "depth": D, "topk": K},
+        "kernel_ms": round(k_ms, 5),
+        "kernel_ms_p10_p50_p90": [round(float(np.percentile(each, q)), 5) for q in (10, 50, 90)],
+        "kernel_source_hash": kernel_source_hash(),
+        # the pops of one request form one dependent chain: the bound is its latency per node
+        "roofline": {"bound": "latency", "achieved": round(k_ms * 1e6 / N, 2), "peak": None,
+                     "unit": "ns per node (serial pops of one request)", "frac": None, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle_tree.best_first_tree(lp, cand, N)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or dt * (reps + 1) / reps > 30.0:
+                break
+        line["cpu_baseline"] = {
+            "value": round(reps * B / dt, 3), "unit": "requests/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} whole launch(es) of the same inputs in {dt:.2f} s (plain Python heapq, one thread)"}
+    return line
+
+
 # HBM traffic of the attention kernel per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # summarised under profiles/.  The summary records a hash of the kernel sources it was taken
 # on; when the sources have changed since, the figure no longer describes this kernel and
@@ -400,7 +469,8 @@ def kernel_source_hash() -> str:
     import glob
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_verify_mla_02_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+    # the sources the attention kernel is compiled from (other kernels do not change it)
+    for f in [os.path.join(csrc, "verify_attn.hip"), os.path.join(csrc, "kdt_internal.h")]:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -434,9 +504,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="attention launches timed after flushing L2 and MALL (0 to skip)")
-    ap.add_argument("--row", default="verify", choices=["verify", "accept", "compact"],
-                    help="verify: the tree-verify attention step (default); accept / compact: the greedy "
-                         "tree-accept or the KV compaction kernel alone, on the workload's trees and lengths")
+    ap.add_argument("--row", default="verify", choices=["verify", "accept", "compact", "tree"],
+                    help="verify: the tree-verify attention step (default); accept / compact / tree: the greedy "
+                         "tree-accept, the KV compaction or the best-first tree builder kernel alone, on the "
+                         "workload's trees and lengths")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -452,6 +523,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_direction": n, "launches": args.steps}), flush=True)
+        return
+    if args.row == "tree":
+        print(json.dumps(run_tree_row(args)), flush=True)
         return
     if args.row != "verify":
         print(json.dumps(run_next_row(args)), flush=True)

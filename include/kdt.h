@@ -189,6 +189,32 @@ int kdt_tree_accept(const int32_t *parents, const int32_t *tokens, const int32_t
                     int32_t *accept_len, int32_t *bonus, void *stream);
 
 /*
+ * kdt_build_tree -- best-first draft-tree construction, the step before verification: the
+ * engine's GPU best-first tree builder, which replaced a per-request CPU heap ("Validating the
+ * Native Engine", section "The Broader Context").  The drafter gives, per depth and top-k
+ * slot, a log probability sorted descending and a token id ("The Capstone Validation",
+ * section "What the Test Actually Validated").
+ *   logp     [B, D, K] float32, device: row (b, d) holds depth d+1's K log probabilities,
+ *            best first.  Must not hold NaN.
+ *   cand     [B, D, K] int32, device: the matching token ids.
+ *   max_depth D >= 1, topk K >= 1, D * K <= 8192; num_nodes N in [1, 256].
+ *   parents  [B, N] int32, device, out: node i's parent (-1 at depth 1); parent < child, ready
+ *            for kdt_build_visibility / kdt_tree_verify_prepare.
+ *   tokens, depth, rank [B, N] int32, device, out, each nullable: node i's token id, depth
+ *            (1-based) and rank within its depth's K slots.
+ * A node is a rank path (k_1..k_d) scored by the fp32 sum of its log probabilities, added one
+ * depth at a time.  Starting from the depth-1 rank-0 path, each step takes the best frontier
+ * path (equal scores: the earliest pushed) as node i, then pushes its next sibling (rank + 1,
+ * if below K) and its first child (rank 0 one level deeper, if below D), in that order.  With
+ * rows sorted descending the nodes are the N best rank paths, in score order.  A request with
+ * fewer than N paths in total (K + K^2 + ... + K^D < N) gets -2 in every output of the rows
+ * it cannot fill.  Everything is checked on the host; nothing is written to device status.
+ */
+int kdt_build_tree(const float *logp, const int32_t *cand, int32_t batch, int32_t max_depth, int32_t topk,
+                   int32_t num_nodes, int32_t *parents, int32_t *tokens, int32_t *depth, int32_t *rank,
+                   void *stream);
+
+/*
  * kdt_kv_compact -- post-verify compaction of the committed cache ("Validating the Native
  * Engine", section "The Broader Context": a KV cache with post-verify compaction): each
  * request's accepted tree rows are committed right after its committed rows.

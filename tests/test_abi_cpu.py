@@ -127,3 +127,20 @@ def test_kv_compact_rejects_bad_arguments_on_host():
     assert b"batch 1" in lib.kdt_last_error()
     d.num_nodes = 300
     assert call() == _lib.KDT_ERR_UNSUPPORTED
+
+
+def test_build_tree_rejects_bad_arguments_on_host():
+    lib = kdt.load()
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced: every call fails before any launch
+
+    def call(lp=fake, cand=fake, B=1, D=8, K=8, N=64, par=fake, tok=None, dep=None, rk=None):
+        return lib.kdt_build_tree(lp, cand, B, D, K, N, par, tok, dep, rk, None)
+    assert call(lp=None) == _lib.KDT_ERR_INVALID_ARG
+    assert call(par=None) == _lib.KDT_ERR_INVALID_ARG
+    assert call(B=0) == _lib.KDT_ERR_INVALID_ARG
+    assert call(D=0) == _lib.KDT_ERR_INVALID_ARG
+    assert call(K=0) == _lib.KDT_ERR_INVALID_ARG
+    assert call(D=2, K=4097) == _lib.KDT_ERR_UNSUPPORTED
+    assert call(N=0) == _lib.KDT_ERR_UNSUPPORTED
+    assert call(N=257) == _lib.KDT_ERR_UNSUPPORTED
+    assert call(tok=ctypes.c_void_p((1 << 20) + 2)) == _lib.KDT_ERR_MISALIGNED

@@ -23,7 +23,7 @@ EXPORTS = [
     "kdt_build_visibility", "kdt_tree_verify_workspace_size", "kdt_tree_verify_attn",
     "kdt_tree_verify_plan", "kdt_tree_verify_prepare", "kdt_tree_verify_attend", "kdt_tree_verify_combine",
     "kdt_tree_verify_num_splits", "kdt_status_string", "kdt_last_error", "kdt_last_status", "kdt_version",
-    "kdt_tree_accept", "kdt_kv_compact",
+    "kdt_tree_accept", "kdt_kv_compact", "kdt_build_tree",
 ]
 
 
@@ -68,6 +68,7 @@ def load() -> ctypes.CDLL:
     lib.kdt_tree_verify_combine.argtypes = [vp, dp, vp, sz, vp]
     lib.kdt_tree_accept.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
     lib.kdt_kv_compact.argtypes = [vp] * 10 + [i64, dp, vp, vp]
+    lib.kdt_build_tree.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.kdt_status_string.restype = ctypes.c_char_p
     lib.kdt_last_error.restype = ctypes.c_char_p
     for name in EXPORTS:
@@ -250,6 +251,27 @@ def tree_accept(parents, tokens, target_next, root_next, path=None, accept_len=N
     _check(load().kdt_tree_accept(_ptr(parents), _ptr(tokens), _ptr(target_next), _ptr(root_next), B, N,
                                   _ptr(path), _ptr(accept_len), _ptr(bonus), _stream(stream)))
     return path, accept_len, bonus
+
+
+def build_tree(logp, cand, num_nodes: int, parents=None, tokens=None, depth=None, rank=None, stream=None):
+    """Best-first draft tree from per-depth top-K log probabilities.
+
+    logp [B, D, K] float32 and cand [B, D, K] int32 on the device; returns (parents, tokens,
+    depth, rank), each [B, num_nodes] int32 (-2 in rows a too small tree cannot fill)."""
+    if logp.dtype != torch.float32 or logp.dim() != 3 or not logp.is_contiguous():
+        raise ValueError("logp must be a contiguous [B, D, K] float32 tensor")
+    if cand.dtype != torch.int32 or cand.shape != logp.shape or not cand.is_contiguous():
+        raise ValueError("cand must be a contiguous int32 tensor shaped like logp")
+    B, D, K = logp.shape
+    outs = []
+    for t in (parents, tokens, depth, rank):
+        if t is None:
+            t = torch.empty((B, num_nodes), dtype=torch.int32, device=logp.device)
+        _int32_2d(t, "tree output")
+        outs.append(t)
+    _check(load().kdt_build_tree(_ptr(logp), _ptr(cand), B, D, K, int(num_nodes), *[_ptr(t) for t in outs],
+                                 _stream(stream)))
+    return tuple(outs)
 
 
 def kv_compact(ckv, krope, cache_lens, tree_ckv, tree_krope, path, accept_len, desc: VerifyDesc, ckv_out,

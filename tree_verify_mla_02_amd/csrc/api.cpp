@@ -264,6 +264,27 @@ int kdt_tree_accept(const int32_t *parents, const int32_t *tokens, const int32_t
     return ok();
 }
 
+int kdt_build_tree(const float *logp, const int32_t *cand, int32_t batch, int32_t max_depth, int32_t topk,
+                   int32_t num_nodes, int32_t *parents, int32_t *tokens, int32_t *depth, int32_t *rank,
+                   void *stream) {
+    if (!logp || !cand || !parents) return fail(KDT_ERR_INVALID_ARG, "logp, cand and parents may not be NULL");
+    if (batch < 1) return fail(KDT_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+    if (max_depth < 1 || topk < 1) return fail(KDT_ERR_INVALID_ARG, "max_depth and topk must be >= 1");
+    if ((int64_t)max_depth * topk > kdt::kMaxTreeTable)
+        return fail(KDT_ERR_UNSUPPORTED, "max_depth * topk must be at most %d (got %lld)", kdt::kMaxTreeTable,
+                    (long long)max_depth * topk);
+    if (num_nodes < 1 || num_nodes > kdt::kMaxNodes)
+        return fail(KDT_ERR_UNSUPPORTED, "num_nodes must be in [1, %d] (got %d)", kdt::kMaxNodes, num_nodes);
+    const void *ptrs[] = {logp, cand, parents, tokens, depth, rank};
+    for (const void *q : ptrs)
+        if ((uintptr_t)q & 3u) return fail(KDT_ERR_MISALIGNED, "arrays must be 4-byte aligned");
+    if (batch > INT32_MAX / 2) return fail(KDT_ERR_INVALID_ARG, "batch too large for one launch");
+    const hipError_t e = kdt::launch_tree_build(logp, cand, batch, max_depth, topk, num_nodes, parents, tokens,
+                                                depth, rank, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "tree build launch");
+    return ok();
+}
+
 int kdt_kv_compact(const void *ckv_cache, const void *krope_cache, const int32_t *cache_lens, const void *tree_ckv,
                    const void *tree_krope, const int32_t *path, const int32_t *accept_len, void *ckv_out,
                    void *krope_out, int32_t *new_lens, int64_t out_capacity_rows, const kdt_verify_desc *desc,

@@ -19,7 +19,12 @@ constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerTile = kWaves * kRowsPerWave;   // 128
 constexpr int kKeysPerTile = 64;                       // one LDS tile = 64 keys
 constexpr int kMaxNodes = 256;                         // 4 mask words
-constexpr int kMinChunk = 256;                         // a split covers at least 4 tiles
+#ifndef KDT_MIN_CHUNK
+#define KDT_MIN_CHUNK 256
+#endif
+constexpr int kMinChunk = KDT_MIN_CHUNK;               // keys per split at least (a multiple of 64)
+static_assert(kMinChunk % 64 == 0 && kMinChunk >= 64, "whole key tiles per split");
+constexpr int kMaxTreeTable = 8192;                    // tree builder: D * K log probabilities in LDS
 
 struct Geometry {
     int64_t rows;          // R = N * H query rows per request
@@ -85,6 +90,8 @@ hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st);
 hipError_t launch_accept(const int32_t *parents, const int32_t *tokens, const int32_t *target_next,
                          const int32_t *root_next, int B, int N, int32_t *path, int32_t *accept_len,
                          int32_t *bonus, hipStream_t st);
+hipError_t launch_tree_build(const float *logp, const int32_t *cand, int B, int D, int K, int N,
+                             int32_t *parents, int32_t *tokens, int32_t *depth, int32_t *rank, hipStream_t st);
 hipError_t launch_compact(const void *ckv, const void *krope, const int32_t *cache_lens, const void *tree_ckv,
                           const void *tree_krope, const int32_t *path, const int32_t *accept_len, void *ckv_out,
                           void *krope_out, int32_t *new_lens, int64_t capacity, const kdt_verify_desc &d,
