@@ -11,23 +11,28 @@
 // below D), in that order.  A path's score is its prefix's score plus one fp32 log
 // probability, rounded once per step.
 //
-// The search is sequential per request, so one wave builds one request.  Frontier entries are
-// numbered in push order (entry e = the e-th push; at most 1 + 2N of them) and entry e belongs
-// to lane e % 64, slot e / 64.  Each lane keeps its slots' order keys in registers and its own
-// best; a pop is a wave arg-max over the 64 lane bests (DPP inside rows of 16 lanes, lane reads
-// across rows), so no step touches memory on the way to the next decision.  The order key is
-// the score's fp32 pattern mapped to an unsigned integer that sorts like the float (zeroes of
-// either sign map to one key); equal keys go to the lower entry number = the earlier push.
+// The search is sequential per request, so one wave builds one request.  A prefix's child of
+// rank r + 1 is pushed only when its child of rank r is popped (rank 0: when the prefix itself
+// is), so the frontier holds at most one entry per prefix: its next unpopped child.  It is
+// therefore kept as one slot per prefix p (p = -1 for depth 1, else a popped node), holding
+// that child's rank r, the prefix's score and the entry's score; a pop moves the slot of the
+// popped child's prefix on to rank r + 1 and opens the slot of the new node (its rank-0
+// child).  Slot j = p + 1 lives in lane j % 64, register slot j / 64 (at most 5 per lane for
+// N <= 256).  Equal scores go to the earlier push; an entry's push number is counted exactly
+// as a heap would count it (a next sibling is pushed before the first child).  A pop is a wave
+// max over the 64 lane bests (DPP inside rows of 16 lanes, lane reads across rows) and a
+// ballot for the lane that holds it; the winner's fields come back by lane reads, and one LDS
+// read of the log-probability table gives the two new entry scores.  The order key is the
+// score's fp32 pattern mapped to an unsigned integer that sorts like the float (zeroes of
+// either sign map to one key).
 #include "kdt_internal.h"
 
 namespace kdt {
 
-constexpr int kTreeSlots = (1 + 2 * kMaxNodes + 63) / 64;   // 9 entries per lane at most
-
 // Unsigned key that orders like the float value (-0 and +0 equal); 0 is below every score.
-__device__ __forceinline__ uint32_t order_key(float s) {
-    if (s == 0.0f) s = 0.0f;
-    const uint32_t u = __float_as_uint(s);
+__device__ __forceinline__ uint32_t order_key(float v) {
+    if (v == 0.0f) v = 0.0f;
+    const uint32_t u = __float_as_uint(v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
@@ -47,13 +52,25 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
     return op(op(r0, r1), op(r2, r3));
 }
 
-struct TreeEntry {          // one frontier entry, in LDS
-    float score;            // the path's score
-    float base;             // its prefix node's score (0 at depth 1): a next sibling adds to it
-    int32_t prefix;         // prefix node index, -1 at depth 1
-    int32_t dk;             // depth index d (0-based) << 16 | rank k
-};
+// f(0), ..., f(S-1) with compile-time indices (keeps per-slot arrays in registers).
+template <int I, int S, class F>
+__device__ __forceinline__ void each_slot(F &&f) {
+    if constexpr (I < S) {
+        f(std::integral_constant<int, I>{});
+        each_slot<I + 1, S>(f);
+    }
+}
 
+// Value of register slot `slot` (uniform) of lane `lane` (uniform), for every lane.
+template <int S>
+__device__ __forceinline__ uint32_t fetch(const uint32_t (&v)[S], int slot, int lane) {
+    uint32_t x = v[0];
+    each_slot<1, S>([&](auto I) { x = slot == I.value ? v[I.value] : x; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+
+// S = register slots per lane: ceil((N + 1) / 64).
+template <int S>
 __global__ __launch_bounds__(64) void tree_build_kernel(const float *__restrict__ logp,
                                                         const int32_t *__restrict__ cand, int D, int K,
                                                         int N, int32_t *__restrict__ parents,
@@ -61,7 +78,6 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const float *__restrict_
                                                         int32_t *__restrict__ depth,
                                                         int32_t *__restrict__ rank) {
     extern __shared__ float s_lp[];                     // [D*K] this request's log probabilities
-    __shared__ TreeEntry s_ent[64 * kTreeSlots];
     __shared__ int32_t s_npar[kMaxNodes], s_ndk[kMaxNodes];
     const int64_t b = blockIdx.x;
     const int lane = threadIdx.x;
@@ -69,69 +85,85 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const float *__restrict_
     for (int i = lane; i < DK; i += 64) s_lp[i] = logp[b * DK + i];
     __syncthreads();
 
-    // keys of this lane's entries (entry e lives in lane e % 64, slot e / 64), as scalars so
-    // that they stay in registers; 0 = no entry
-    uint32_t k0 = 0, k1 = 0, k2 = 0, k3 = 0, k4 = 0, k5 = 0, k6 = 0, k7 = 0, k8 = 0;
-    static_assert(kTreeSlots == 9, "one register per slot");
-    uint32_t best_key = 0u;          // this lane's best entry key and slot
+    // this lane's slots: entry order key (0 = none), push number, entry score, prefix score,
+    // and (children's depth index << 16 | next rank)
+    uint32_t key[S], tie[S], esc[S], base[S], dr[S];
+    each_slot<0, S>([&](auto I) { key[I.value] = tie[I.value] = esc[I.value] = base[I.value] = dr[I.value] = 0u; });
+    uint32_t best_key = 0u, best_tie = 0u;   // this lane's best slot by (key desc, push asc)
     int best_slot = 0;
-    int count = 0;                   // entries pushed so far (uniform)
+    if (lane == 0) {                          // slot 0: prefix -1, entry = depth-1 rank 0
+        const float e = s_lp[0];
+        key[0] = best_key = order_key(e);
+        esc[0] = __float_as_uint(e);
+    }
+    int pushes = 1;
 
-#define KDT_SET_SLOT(slot, v)                                                                   \
-    do {                                                                                        \
-        const int s_ = (slot);                                                                  \
-        const uint32_t v_ = (v);                                                                \
-        k0 = s_ == 0 ? v_ : k0; k1 = s_ == 1 ? v_ : k1; k2 = s_ == 2 ? v_ : k2;                 \
-        k3 = s_ == 3 ? v_ : k3; k4 = s_ == 4 ? v_ : k4; k5 = s_ == 5 ? v_ : k5;                 \
-        k6 = s_ == 6 ? v_ : k6; k7 = s_ == 7 ? v_ : k7; k8 = s_ == 8 ? v_ : k8;                 \
-    } while (0)
-    // push entry number `count` (uniform); its owner lane records the key
-#define KDT_PUSH(score_, base_, prefix_, d_, k_)                                                \
-    do {                                                                                        \
-        const float sc_ = (score_);                                                             \
-        const int e_ = count++;                                                                 \
-        const uint32_t kk_ = order_key(sc_);                                                    \
-        if (lane == 0) s_ent[e_] = TreeEntry{sc_, (base_), (prefix_), ((d_) << 16) | (k_)};     \
-        if (lane == (e_ & 63)) {                                                                \
-            KDT_SET_SLOT(e_ >> 6, kk_);                                                         \
-            if (kk_ > best_key) { /* a later push never beats an equal earlier one */           \
-                best_key = kk_;                                                                 \
-                best_slot = e_ >> 6;                                                            \
-            }                                                                                   \
-        }                                                                                       \
-    } while (0)
-
-    KDT_PUSH(s_lp[0], 0.0f, -1, 0, 0);
     int n = 0;
     for (; n < N; n++) {
         const uint32_t top = wave_reduce_u32<true>(best_key);
         if (top == 0u) break;                                       // the frontier is empty
-        const uint32_t cand_e = best_key == top ? (uint32_t)(best_slot * 64 + lane) : 0xFFFFFFFFu;
-        const int e = (int)wave_reduce_u32<false>(cand_e);          // earliest push among the best
-        __syncthreads();                                            // lane 0's entry write is visible
-        const TreeEntry t = s_ent[e];
-        const int d = t.dk >> 16, k = t.dk & 0xFFFF;
+        // the lane holding the best entry; only equal best scores in several lanes (rare)
+        // need the push numbers compared
+        uint64_t m = __ballot(best_key == top);
+        if (__builtin_popcountll(m) > 1) {
+            const uint32_t t_min = wave_reduce_u32<false>(best_key == top ? best_tie : 0xFFFFFFFFu);
+            m = __ballot(best_key == top && best_tie == t_min);   // push numbers are unique
+        }
+        const int jl = __builtin_ctzll(m);
+        const int js = __builtin_amdgcn_readlane(best_slot, jl);
+        const int j = js * 64 + jl;
+        const float score = __uint_as_float(fetch<S>(esc, js, jl));
+        const float pbase = __uint_as_float(fetch<S>(base, js, jl));
+        const uint32_t pdr = fetch<S>(dr, js, jl);
+        const int d = (int)(pdr >> 16), r = (int)(pdr & 0xFFFFu);
+        // the two entries this pop pushes: the next sibling, then the first child
+        const bool sib = r + 1 < K, child = d + 1 < D;
+        const float lp_sib = s_lp[d * K + (sib ? r + 1 : r)];
+        const float lp_child = s_lp[(child ? d + 1 : d) * K];
         if (lane == 0) {
-            s_npar[n] = t.prefix;
-            s_ndk[n] = t.dk;
+            s_npar[n] = j - 1;
+            s_ndk[n] = (int)pdr;
         }
-        if (lane == (e & 63)) {                                     // retire the entry, rescan the lane
-            KDT_SET_SLOT(e >> 6, 0u);
-            const uint32_t ks[kTreeSlots] = {k0, k1, k2, k3, k4, k5, k6, k7, k8};
+        const uint32_t t_sib = (uint32_t)pushes;
+        pushes += sib ? 1 : 0;
+        const uint32_t t_child = (uint32_t)pushes;
+        pushes += child ? 1 : 0;
+        const float e_sib = pbase + lp_sib;
+        const float e_child = score + lp_child;
+        const uint32_t k_sib = sib ? order_key(e_sib) : 0u;
+        const uint32_t k_child = child ? order_key(e_child) : 0u;
+        // slot j moves on to rank r + 1; slot n + 1 opens with the new node's rank-0 child
+        const int jn = n + 1, jnl = jn & 63, jns = jn >> 6;
+        each_slot<0, S>([&](auto I) {
+            constexpr int i = I.value;
+            if (lane == jl && i == js) {
+                key[i] = k_sib;
+                tie[i] = t_sib;
+                esc[i] = __float_as_uint(e_sib);
+                dr[i] = pdr + 1u;
+            }
+            if (lane == jnl && i == jns) {
+                key[i] = k_child;
+                tie[i] = t_child;
+                esc[i] = __float_as_uint(e_child);
+                base[i] = __float_as_uint(score);
+                dr[i] = (uint32_t)(d + 1) << 16;
+            }
+        });
+        if (lane == jl || lane == jnl) {                            // rescan the changed lanes
             best_key = 0u;
+            best_tie = 0u;
             best_slot = 0;
-#pragma unroll
-            for (int s = 0; s < kTreeSlots; s++)
-                if (ks[s] > best_key) {
-                    best_key = ks[s];
-                    best_slot = s;
+            each_slot<0, S>([&](auto I) {
+                constexpr int i = I.value;
+                if (key[i] > best_key || (key[i] == best_key && key[i] != 0u && tie[i] < best_tie)) {
+                    best_key = key[i];
+                    best_tie = tie[i];
+                    best_slot = i;
                 }
+            });
         }
-        if (k + 1 < K) KDT_PUSH(t.base + s_lp[d * K + k + 1], t.base, t.prefix, d, k + 1);
-        if (d + 1 < D) KDT_PUSH(t.score + s_lp[(d + 1) * K], t.score, n, d + 1, 0);
     }
-#undef KDT_PUSH
-#undef KDT_SET_SLOT
     __syncthreads();
     // outputs: nodes [0, n), then -2 for the rows a too small tree could not fill
     for (int i = lane; i < N; i += 64) {
@@ -153,7 +185,18 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const float *__restrict_
 hipError_t launch_tree_build(const float *logp, const int32_t *cand, int B, int D, int K, int N,
                              int32_t *parents, int32_t *tokens, int32_t *depth, int32_t *rank, hipStream_t st) {
     const size_t lds = (size_t)D * K * sizeof(float);
-    tree_build_kernel<<<(unsigned)B, 64, lds, st>>>(logp, cand, D, K, N, parents, tokens, depth, rank);
+    const int slots = (N + 1 + 63) / 64;
+    auto go = [&](auto kernel) {
+        kernel<<<(unsigned)B, 64, lds, st>>>(logp, cand, D, K, N, parents, tokens, depth, rank);
+    };
+    switch (slots) {
+        case 1: go(tree_build_kernel<1>); break;
+        case 2: go(tree_build_kernel<2>); break;
+        case 3: go(tree_build_kernel<3>); break;
+        case 4: go(tree_build_kernel<4>); break;
+        case 5: go(tree_build_kernel<5>); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
