@@ -364,9 +364,10 @@ def run_next_row(args):
                    "batch": B, "nodes": N},
         "kernel_ms": round(k_ms, 5),
         "kernel_ms_p10_p50_p90": [round(float(np.percentile(each, q)), 5) for q in (10, 50, 90)],
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash("tree_accept" if args.row == "accept" else "kv_compact"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": recorded_traffic(sp.name, "kv_compact") if args.row == "compact" else None},
     }
     if not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))
@@ -441,7 +442,7 @@ def run_tree_row(args):
                    "batch": B, "nodes": N, "depth": D, "topk": K},
         "kernel_ms": round(k_ms, 5),
         "kernel_ms_p10_p50_p90": [round(float(np.percentile(each, q)), 5) for q in (10, 50, 90)],
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash("tree_build"),
         # the pops of one request form one dependent chain: the bound is its latency per node
         "roofline": {"bound": "latency", "achieved": round(k_ms * 1e6 / N, 2), "peak": None,
                      "unit": "ns per node (serial pops of one request)", "frac": None, "traffic": None},
@@ -464,20 +465,29 @@ def run_tree_row(args):
 # summarised under profiles/.  The summary records a hash of the kernel sources it was taken
 # on; when the sources have changed since, the figure no longer describes this kernel and
 # `traffic` is reported as null.
-def kernel_source_hash() -> str:
+# Sources each kernel is compiled from (a change to any other file leaves it as it was).
+KERNEL_SOURCES = {
+    "verify_attn": ["verify_attn.hip", "kdt_internal.h"],
+    "kv_compact": ["accept.hip", "kdt_internal.h"],
+    "tree_accept": ["accept.hip", "kdt_internal.h"],
+    "tree_build": ["tree_build.hip", "kdt_internal.h"],
+}
+
+
+def kernel_source_hash(kernel: str = "verify_attn") -> str:
     import hashlib
-    import glob
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_verify_mla_02_amd", "csrc")
-    # the sources the attention kernel is compiled from (other kernels do not change it)
-    for f in [os.path.join(csrc, "verify_attn.hip"), os.path.join(csrc, "kdt_internal.h")]:
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
-    path = os.path.join(ROOT, "profiles", f"verify_attn_{workload}_hbm_traffic.md")
+def recorded_traffic(workload: str, kernel: str = "verify_attn"):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_hbm_traffic.md, or None when
+    there is no summary or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -486,7 +496,7 @@ def recorded_traffic(workload: str):
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].split(": ", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_hash") != kernel_source_hash():
+    if fields.get("kernel_source_hash") != kernel_source_hash(kernel):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])

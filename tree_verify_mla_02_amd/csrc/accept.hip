@@ -67,13 +67,16 @@ hipError_t launch_accept(const int32_t *parents, const int32_t *tokens, const in
 
 // ------------------------------------------------------------------------------ compaction
 // New packed cache: request b's committed rows, then its accepted rows in path order, requests
-// packed in request order.  Workgroup (b, c) copies rows [c*kRows, (c+1)*kRows) of request
-// b's new range.  Each first computes, from all of cache_lens and accept_len, the request's
+// packed in request order.  Workgroup (b, c) copies rows [32pc, 32p(c + 1)) of request b's
+// new range in p passes of 32 rows (p = 1 for small grids, up to 4 for large ones, which
+// spreads each workgroup's length scan over more rows).  Each first computes, from all of cache_lens and accept_len, the request's
 // old and new offsets and whether the lengths are valid.  A bad length anywhere, or more rows
 // than the source bound or the destination capacity, writes nothing; a path entry that names
 // no node leaves that request unwritten; both set KDT_DEV_BAD_ACCEPT.  Rows move as 16-byte
-// chunks, one per thread per step, so a wave reads and writes whole 1 KB runs of a row.
-constexpr int kCompactRows = 32;
+// chunks: a wave copies whole rows, so every load and store instruction covers 1 KB of one
+// row.
+constexpr int kCompactWindow = 32;                 // rows copied per pass of a workgroup
+constexpr int kCompactMaxPasses = 4;               // passes per workgroup at most
 
 struct CompactArgs {
     const char *ckv, *krope;             // source rows (element strides below)
@@ -86,6 +89,7 @@ struct CompactArgs {
     int lat_chunks, rope_chunks;         // 16-byte chunks per row of each part
     int64_t max_len, total_len, capacity;
     int in_place;                        // destination == source (one request): copy appended rows only
+    int passes;                          // 32-row passes per workgroup
 };
 
 __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
@@ -139,44 +143,60 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
         return;
     }
     if (c == 0 && tid == 0) a.new_lens[b] = (int32_t)(L + A);
-    const int64_t r0 = (int64_t)c * kCompactRows;
-    const int64_t r_end = (r0 + kCompactRows < L + A) ? r0 + kCompactRows : L + A;
     const int cpr = a.lat_chunks + a.rope_chunks;
-    const int64_t first = a.in_place ? (r0 > L ? r0 : L) : r0;   // in place: committed rows stay
-    const int n = r_end > first ? (int)(r_end - first) * cpr : 0;
-    // chunk e of the range: row first + e / cpr, chunk e % cpr; four per thread in flight
-    auto addr = [&](int e, const char *&src, char *&dst) {
-        const int64_t r = first + e / cpr;
-        const int ch = e % cpr;
-        const bool lat = ch < a.lat_chunks;
-        const int cc = lat ? ch : ch - a.lat_chunks;
-        if (r < L) {
-            const int64_t row = old_off + r;
-            src = (lat ? a.ckv + row * a.ckv_stride : a.krope + row * a.krope_stride) + cc * 16;
-        } else {
-            const int64_t node = (int64_t)b * a.N + a.path[(int64_t)b * a.N + (r - L)];
-            src = (lat ? a.tckv + node * a.tckv_stride : a.tkrope + node * a.tkrope_stride) + cc * 16;
+    for (int pass = 0; pass < a.passes; pass++) {
+        const int64_t r0 = ((int64_t)c * a.passes + pass) * kCompactWindow;
+        if (r0 >= L + A) break;
+        const int64_t r_end = (r0 + kCompactWindow < L + A) ? r0 + kCompactWindow : L + A;
+        const int64_t first = a.in_place ? (r0 > L ? r0 : L) : r0;   // in place: committed rows stay
+        // Wave w copies rows first + w, first + w + 4, ... (kWaveRows of them at most); lane l
+        // moves 16-byte chunks l, l + 64, ... of each row.  All of a wave's loads are issued before
+        // its stores, so every lane keeps up to kWaveRows * kChunksPerLane loads in flight.
+        constexpr int kWaveRows = kCompactWindow / 4;
+        constexpr int kChunksPerLane = 3;                  // rows of at most 192 chunks (3 KB)
+        // Row bases are wave-uniform: the path entries of the wave's accepted rows are read
+        // before any data load, so the data loads are issued back to back with no wait between.
+        const int w = __builtin_amdgcn_readfirstlane(wave);
+        const char *sl[kWaveRows], *sr[kWaveRows];
+        char *dl[kWaveRows], *dr[kWaveRows];
+        bool live[kWaveRows];
+        int32_t node[kWaveRows];
+    #pragma unroll
+        for (int i = 0; i < kWaveRows; i++) {
+            const int64_t r = first + w + 4 * i;
+            live[i] = r < r_end;
+            node[i] = (live[i] && r >= L) ? a.path[(int64_t)b * a.N + (r - L)] : 0;
         }
-        const int64_t drow = new_off + r;
-        dst = (lat ? a.ockv + drow * a.ckv_stride : a.okrope + drow * a.krope_stride) + cc * 16;
-    };
-    constexpr int U = 4;
-    for (int base = tid; base < n; base += U * (int)blockDim.x) {
-        uint4 x[U];
-        char *dst[U];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int e = base + u * (int)blockDim.x;
-            const char *src = nullptr;
-            dst[u] = nullptr;
-            if (e < n) {
-                addr(e, src, dst[u]);
-                x[u] = *(const uint4 *)src;
+    #pragma unroll
+        for (int i = 0; i < kWaveRows; i++) {
+            const int64_t r = first + w + 4 * i;
+            const int64_t crow = old_off + r, trow = (int64_t)b * a.N + node[i], drow = new_off + r;
+            const bool cached = r < L;
+            sl[i] = cached ? a.ckv + crow * a.ckv_stride : a.tckv + trow * a.tckv_stride;
+            sr[i] = cached ? a.krope + crow * a.krope_stride : a.tkrope + trow * a.tkrope_stride;
+            dl[i] = a.ockv + drow * a.ckv_stride;
+            dr[i] = a.okrope + drow * a.krope_stride;
+        }
+        uint4 x[kWaveRows][kChunksPerLane];
+    #pragma unroll
+        for (int i = 0; i < kWaveRows; i++)
+    #pragma unroll
+            for (int j = 0; j < kChunksPerLane; j++) {
+                const int ch = lane + 64 * j;
+                const bool lat = ch < a.lat_chunks;
+                const char *src = lat ? sl[i] + ch * 16 : sr[i] + (ch - a.lat_chunks) * 16;
+                x[i][j] = make_uint4(0u, 0u, 0u, 0u);
+                if (live[i] && ch < cpr) x[i][j] = *(const uint4 *)src;
             }
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++)
-            if (dst[u]) *(uint4 *)dst[u] = x[u];
+    #pragma unroll
+        for (int i = 0; i < kWaveRows; i++)
+    #pragma unroll
+            for (int j = 0; j < kChunksPerLane; j++) {
+                const int ch = lane + 64 * j;
+                const bool lat = ch < a.lat_chunks;
+                char *dst = lat ? dl[i] + ch * 16 : dr[i] + (ch - a.lat_chunks) * 16;
+                if (live[i] && ch < cpr) *(uint4 *)dst = x[i][j];
+            }
     }
 }
 
@@ -209,8 +229,12 @@ hipError_t launch_compact(const void *ckv, const void *krope, const int32_t *cac
     a.total_len = d.total_cache_len;
     a.capacity = capacity;
     a.in_place = ckv_out == ckv;
+    if (a.lat_chunks + a.rope_chunks > 192) return hipErrorInvalidValue;   // 3 chunks per lane and row
     const int64_t rows_max = d.max_cache_len + d.num_nodes;
-    const dim3 grid((unsigned)d.batch, (unsigned)((rows_max + kCompactRows - 1) / kCompactRows));
+    const int64_t windows = (rows_max + kCompactWindow - 1) / kCompactWindow;
+    int64_t p = (int64_t)d.batch * windows / 2048;           // keep about 2048 workgroups or more
+    a.passes = (int)(p < 1 ? 1 : p > kCompactMaxPasses ? kCompactMaxPasses : p);
+    const dim3 grid((unsigned)d.batch, (unsigned)((windows + a.passes - 1) / a.passes));
     compact_kernel<<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
 }
