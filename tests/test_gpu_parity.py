@@ -77,6 +77,19 @@ SMALL = {
     "f32_split": (workloads.Spec("f32s", 47, 1, 8, 4, 64, 16, "f32", 5000, tree="random"), None),
     "star": (workloads.Spec("star", 48, 2, 12, 8, 512, 64, "bf16", 130, tree="star"), None),
     "chain_short": (workloads.Spec("chs", 49, 1, 16, 64, 512, 64, "bf16", 1000, tree="chain"), None),
+    # at most 64 rows per request (the decode-shape kernel): one node x 64 heads over ragged
+    # lengths, an empty cache and tails of one key; 40 rows (a partial second row half); a
+    # 60-node tree of one head (tree keys in both 32-key halves of the tile); outliers; and
+    # enough requests that keys are not split (outputs written by the attention kernel itself)
+    "dec_ragged": (workloads.Spec("dec_r", 60, 5, 1, 64, 512, 64, "bf16", None, ragged=(0, 3000), tree="chain"),
+                   [0, 1, 65, 1000, 2999]),
+    "dec_rows40": (workloads.Spec("dec_40", 61, 2, 5, 8, 512, 64, "bf16", None, ragged=(1, 1500), tree="random"),
+                   [1, 1500]),
+    "dec_tree60": (workloads.Spec("dec_t60", 62, 1, 60, 1, 512, 64, "bf16", 700, depth=8, topk=8), None),
+    "dec_outliers": (workloads.Spec("dec_o", 63, 2, 1, 64, 512, 64, "bf16", 5000, tree="chain", outlier_p=0.01),
+                     None),
+    "dec_unsplit": (workloads.Spec("dec_u", 64, 600, 1, 64, 512, 64, "bf16", None, ragged=(1, 200), tree="chain"),
+                    None),
 }
 
 

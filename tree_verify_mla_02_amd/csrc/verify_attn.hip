@@ -1104,6 +1104,287 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     }
 }
 
+// ------------------------------------------------------------------------------ decode shape
+// Requests of at most 64 query rows (a decode step: one node x up to 64 heads).  With the
+// 128-row workgroup above half of the rows would be empty, and every wave would still issue
+// the 200 MFMAs of a 64-key tile: one CU's matrix pipes, not HBM, would bound the key stream.
+// Here a workgroup takes the request's 64 rows and wave w = (key half kh, row half rh) takes
+// rows 32*rh .. +31 and keys 32*kh .. +31 of every tile: 36 QK + 64 P.V MFMAs per tile and wave
+// instead of 72 + 128, so a tile costs each SIMD about half the time.  Each wave keeps its own
+// online softmax (m, l, O) over its key half; at the end the two key halves of a row half are
+// merged through LDS, and the merged wave writes the output or the split partial exactly as the
+// 128-row kernel's wave rh would (the combine is shared).  Same unit records, tile copies, LDS
+// layout, fragment patterns and precision (P as bf16 hi + lo) as the 128-row kernel.
+
+// S^T of one 32-key block x this wave's 32 rows: a chain of NQ MFMA 32x32x16 on one
+// accumulator, K fragments read QD steps ahead (pq already points at the wave's block).
+template <class Sh, int NQ>
+__device__ __forceinline__ void qk_block(const LDS_AS char *const (&pq)[Sh::CB / 2], const bf16x8 (&q)[NQ],
+                                         f32x16 &acc) {
+    constexpr int PAT = Sh::CB / 2;
+    constexpr int QD = NQ > 5 ? 5 : NQ - 1, NS = QD + 1;
+    static_assert(QD >= 1, "chain of at least two MFMAs");
+    bf16x8 kf[NS];
+    auto read = [&](auto G) {
+        constexpr int g = decltype(G)::value;
+        ds_read_k<(g / PAT) * 1024>(kf[g % NS], pq[g % PAT]);
+    };
+    static_for<0, QD>(read);
+    static_for<0, NQ>([&](auto G) {
+        constexpr int g = decltype(G)::value;
+        constexpr int issued = (g + QD < NQ) ? g + QD : NQ;
+        constexpr int after = issued - g - 1;
+        if constexpr (g == 0)
+            mfma_s_first<after>(acc, kf[g % NS], q[g]);
+        else if constexpr (g == NQ - 1)
+            mfma_s_last<after>(acc, kf[g % NS], q[g]);
+        else
+            mfma_s_next<after>(acc, kf[g % NS], q[g]);
+        if constexpr (g + QD < NQ) read(IntC<g + QD>{});
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+// O^T += V^T P^T over one 32-key block: 2 x 16-key steps x NT16 column tiles x (hi, lo) = 4*NT16
+// MFMAs; vbuf already points at the wave's block.  fill(m) runs after MFMA m.
+template <class Sh, int NT16, class F>
+__device__ __forceinline__ void pv_block(const LDS_AS char *vbuf, const u32x4 (&phi)[2], const u32x4 (&plo)[2],
+                                         f32x16 (&o)[NT16], const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1][2],
+                                         F &&fill) {
+    constexpr int NSTEP = 2 * NT16;     // (h16, t16) pairs
+    constexpr int PD = 4;
+    auto load = [&](int st) {
+        const int h16 = st / NT16, t16 = st % NT16;
+        const int j = (4 * t16 % Sh::CB) / 4, cg_off = (4 * t16 / Sh::CB) * 1024 + key_off<Sh>(16 * h16);
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vbuf + pv_base[j][0] + cg_off));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vbuf + pv_base[j][1] + cg_off));
+        return (bf16x8)__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vf[PD];
+#pragma unroll
+    for (int j = 0; j < PD; j++) vf[j] = load(j);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, NSTEP / 2>([&](auto S2) {
+        constexpr int st = 2 * decltype(S2)::value;
+        constexpr int h16 = st / NT16, t16 = st % NT16, m = 2 * st;
+        o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], __builtin_bit_cast(bf16x8, phi[h16]), o[t16], 0, 0, 0);
+        fill(IntC<m>{});
+        __builtin_amdgcn_sched_barrier(0);
+        o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], __builtin_bit_cast(bf16x8, phi[h16]), o[t16 + 1], 0, 0, 0);
+        fill(IntC<m + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+        o[t16] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st % PD], __builtin_bit_cast(bf16x8, plo[h16]), o[t16], 0, 0, 0);
+        if constexpr (st + PD < NSTEP) vf[st % PD] = load(st + PD);
+        fill(IntC<m + 2>{});
+        __builtin_amdgcn_sched_barrier(0);
+        o[t16 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[(st + 1) % PD], __builtin_bit_cast(bf16x8, plo[h16]), o[t16 + 1], 0, 0, 0);
+        if constexpr (st + 1 + PD < NSTEP) vf[(st + 1) % PD] = load(st + 1 + PD);
+        fill(IntC<m + 3>{});
+        __builtin_amdgcn_sched_barrier(0);
+    });
+}
+
+template <int DC, int DR>
+__global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
+    using T = __bf16;
+    using Sh = Shape<T, DC, DR>;
+    constexpr int NT16 = DC / 32;
+    constexpr int NQ = Sh::D / 16;
+    static_assert(Sh::BF16 && Sh::CB == 8, "bf16 rows of 8-chunk LDS blocks");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * Sh::TILE_BYTES];
+    static_assert(2 * 64 * 256 * 4 + 2 * 64 * 8 <= 2 * Sh::TILE_BYTES, "merge buffers fit in the tile buffers");
+
+    const Unit unit = a.units[blockIdx.x];
+    if (unit.b < 0) return;
+    const int b = unit.b, s = unit.s, sb = unit.sb;     // one row tile: unit.rt == 0
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rh = wave & 1, kh = wave >> 1;            // row half, key half
+    const int half = lane >> 5;
+    const int64_t R = a.R;                              // <= 64 (checked by the launcher)
+
+    const int64_t r = (int64_t)rh * kRowsPerWave + (lane & 31);
+    const bool row_ok = r < R;
+    const int64_t rc = row_ok ? r : R - 1;
+    const int node = (int)(rc / a.H);
+
+    const int64_t k0 = unit.k0, k1 = unit.k1;
+    const int n_cache = k1 > k0 ? (int)(((k1 - k0) + kKeysPerTile - 1) / kKeysPerTile) : 0;
+    const int n_tree = (s == 0) ? (a.N + kKeysPerTile - 1) / kKeysPerTile : 0;
+    const int n_tiles = n_cache + n_tree;
+    const int64_t cache_row0 = unit.row0;
+
+    using Dma = TileDma<Sh, T>;
+    auto dma_setup = [&](Dma &d, int t, int bsel) {
+        LDS_AS char *buf = (LDS_AS char *)smem + bsel * Sh::TILE_BYTES;
+        if (t < n_cache) {
+            const int64_t left = k1 - k0 - (int64_t)t * kKeysPerTile;
+            d.setup(buf, (const T *)a.ckv, a.ckv_stride, (const T *)a.krope, a.krope_stride,
+                    cache_row0 + (int64_t)t * kKeysPerTile, left < kKeysPerTile ? (int)left : kKeysPerTile, wave,
+                    lane);
+        } else {
+            const int tt = t - n_cache;
+            const int left = a.N - tt * kKeysPerTile;
+            d.setup(buf, (const T *)a.tckv, a.tckv_stride, (const T *)a.tkrope, a.tkrope_stride,
+                    (int64_t)b * a.N + (int64_t)tt * kKeysPerTile, left < kKeysPerTile ? left : kKeysPerTile, wave,
+                    lane);
+        }
+    };
+    {
+        Dma d0;
+        dma_setup(d0, 0, 0);
+        d0.template issue<0, Dma::NINST>();
+    }
+    // the request's rows (at most 64) go to buffer 1 together with tile 0: one round trip
+    LDS_AS char *qbuf = (LDS_AS char *)smem + Sh::TILE_BYTES;
+    {
+        Dma dq;
+        dq.setup(qbuf, (const T *)a.q_lat, a.q_lat_stride, (const T *)a.q_rope, a.q_rope_stride, (int64_t)b * R,
+                 (int)R, wave, lane);
+        dq.template issue<0, Dma::NINST>();
+    }
+
+    constexpr int QK_PAT = Sh::CB / 2;
+    constexpr int PV_PAT = Sh::CB / 4;
+    int qk_base[QK_PAT], pv_base[PV_PAT][2];
+#pragma unroll
+    for (int j = 0; j < QK_PAT; j++) qk_base[j] = lds_off<Sh>(lane & 31, 2 * j + half);
+    {
+        const int w = 4 * half + ((lane & 15) >> 2);
+        const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+        for (int j = 0; j < PV_PAT; j++)
+#pragma unroll
+            for (int e = 0; e < 2; e++) pv_base[j][e] = lds_off<Sh>(w + 8 * e, 4 * j + y) + 8 * (lane & 1);
+    }
+    const int blk_off = kh * key_off<Sh>(32);          // this wave's 32-key block inside a tile
+
+    bf16x8 q[NQ];
+    wait_vm_all();
+    __syncthreads();
+    {
+        const LDS_AS char *src = qbuf + key_off<Sh>(32 * rh);
+#pragma unroll
+        for (int kk = 0; kk < NQ; kk++)
+            q[kk] = *(const LDS_AS bf16x8 *)(src + qk_base[kk % QK_PAT] + (kk / QK_PAT) * 1024);
+    }
+    float c_pos = a.scale_log2;
+    if (c_pos <= 0.f) {
+        const bool zero = c_pos == 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NQ; kk++) q[kk] = zero ? q[kk] * (T)0.f : -q[kk];
+        c_pos = zero ? 1.f : -c_pos;
+    }
+
+    f32x16 o[NT16];
+#pragma unroll
+    for (int t = 0; t < NT16; t++) o[t] = (f32x16){};
+    SoftmaxRow sm{-INFINITY, 0.f, c_pos};
+
+    for (int t = 0; t < n_tiles; t++) {
+        wait_vm_all();
+        __syncthreads();                 // tile t is in LDS; every wave is done with tile t-1 (and Q)
+        const LDS_AS char *buf = (const LDS_AS char *)smem + (t & 1) * Sh::TILE_BYTES;
+        const bool is_tree = t >= n_cache;
+        bool need_mask;
+        uint32_t wv = ~0u;
+        if (!is_tree) {
+            const int64_t left = k1 - k0 - (int64_t)t * kKeysPerTile;
+            need_mask = left < kKeysPerTile;
+            if (need_mask) wv = block_bits((1ull << left) - 1ull, kh, half);
+        } else {
+            const int tt = t - n_cache;
+            const int nvalid = a.N - tt * kKeysPerTile;
+            uint64_t vis = a.masks[((int64_t)b * a.N + node) * a.W + tt];
+            if (nvalid < kKeysPerTile) vis &= (1ull << nvalid) - 1ull;
+            wv = block_bits(vis, kh, half);
+            need_mask = true;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // tile t+1 goes into the other buffer (after the last tile: tile t again, as a no-op
+        // for the result, so that the chain below has no branch)
+        const bool more = t + 1 < n_tiles;
+        Dma dn;
+        dma_setup(dn, more ? t + 1 : t, (t + 1) & 1);
+
+        const LDS_AS char *pq[QK_PAT];
+#pragma unroll
+        for (int j = 0; j < QK_PAT; j++) pq[j] = buf + blk_off + qk_base[j];
+        BlockSm bs;
+        qk_block<Sh, NQ>(pq, q, bs.s);
+        if (need_mask) mask_scores(bs.s, wv);
+        // the first half of the softmax (maxima, reference, keys 0..15) before the P.V chain;
+        // keys 16..31 are only read from MFMA 2*NT16 on, so their steps go into the chain
+        constexpr int H1 = kSmPre + 16;
+        static_for<0, H1>([&](auto J) { bs.template stage<J.value>(sm); });
+        if (__ballot(bs.u.alpha != 1.f)) rescale_acc<NT16>(o, bs.u.alpha);
+        constexpr int NC = Dma::NINST;
+        static_assert(2 * (kSmStages - H1) <= 2 * NT16 && 2 * NC <= 4 * NT16, "steps fit in the chain");
+        pv_block<Sh, NT16>(buf + blk_off, bs.phi, bs.plo, o, pv_base, [&](auto M) {
+            constexpr int m = decltype(M)::value;
+            if constexpr (m % 2 == 1 && H1 + m / 2 < kSmStages) bs.template stage<H1 + m / 2>(sm);
+            if constexpr (m % 2 == 0 && m / 2 < NC) dn.template issue<m / 2, m / 2 + 1>();
+        });
+        sm.l = sm.l * bs.u.alpha + bs.sum;
+    }
+    wait_vm_all();                       // no copy may still be landing
+    __syncthreads();                     // every wave is done with the tile buffers
+
+    // ---- merge the two key halves of each row half: waves kh = 1 hand (m, l, O) over
+    float m_run = sm.m_ref, l_run = sm.l;
+    float *xo = (float *)smem;                                        // [rh][16*NT16][64] floats
+    float2 *xml = (float2 *)((char *)smem + 2 * 64 * 16 * NT16 * 4);  // [rh][64]
+    if (kh == 1) {
+#pragma unroll
+        for (int t16 = 0; t16 < NT16; t16++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) xo[(rh * 16 * NT16 + t16 * 16 + i) * 64 + lane] = o[t16][i];
+        xml[rh * 64 + lane] = make_float2(m_run, l_run);
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    {
+        const float2 ml1 = xml[rh * 64 + lane];
+        const float M = fmaxf(m_run, ml1.x);
+        const float c0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+        const float c1 = ml1.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml1.x - M);
+        l_run = l_run * c0 + ml1.y * c1;
+#pragma unroll
+        for (int t16 = 0; t16 < NT16; t16++)
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                o[t16][i] = o[t16][i] * c0 + xo[(rh * 16 * NT16 + t16 * 16 + i) * 64 + lane] * c1;
+        m_run = M;
+    }
+
+    // ---- epilogue, as the 128-row kernel's wave rh: lane holds O^T[t16*32 + (i/4)*8 + 4*half + i%4][row]
+    const float l_tot = row_sum(l_run);
+    if (!row_ok) return;
+    if (sb == 1) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float *dst = a.out + ((int64_t)b * R + r) * DC;
+#pragma unroll
+        for (int t16 = 0; t16 < NT16; t16++)
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const float4 v = make_float4(o[t16][4 * g] * inv, o[t16][4 * g + 1] * inv, o[t16][4 * g + 2] * inv,
+                                             o[t16][4 * g + 3] * inv);
+                *(float4 *)(dst + t16 * 32 + g * 8 + 4 * half) = v;
+            }
+    } else {
+        const int64_t prow = ((int64_t)b * a.S + s) * R + r;
+        const int64_t blk = (((int64_t)b * a.S + s) * a.RT + 0) * kWaves + rh;
+        uint32_t *dst = a.part_o + blk * (kRowsPerWave * DC / 4 * 3) + lane * 3;
+#pragma unroll
+        for (int t16 = 0; t16 < NT16; t16++)
+#pragma unroll
+            for (int g = 0; g < 4; g++)
+                pack24x4(dst + (t16 * 4 + g) * 192, o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2],
+                         o[t16][4 * g + 3]);
+        if (half == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
+    }
+}
+
 // ------------------------------------------------------------------------------ combine
 // out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s, for rows of split
 // requests.  A tile is (request, 32-row group, 32-column tile).  Lane l holds row l % 32 and
@@ -1270,7 +1551,9 @@ hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t
 
 hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units, hipStream_t st) {
     const dim3 grid((unsigned)units), block(256);
-    if (dtype == KDT_BF16 && d_latent == 512 && d_rope == 64)
+    if (dtype == KDT_BF16 && d_latent == 512 && d_rope == 64 && a.R <= 2 * kRowsPerWave)
+        decode_attn_kernel<512, 64><<<grid, block, 0, st>>>(a);
+    else if (dtype == KDT_BF16 && d_latent == 512 && d_rope == 64)
         verify_attn_kernel<__bf16, 512, 64><<<grid, block, 0, st>>>(a);
     else if (dtype == KDT_BF16 && d_latent == 64 && d_rope == 16)
         verify_attn_kernel<__bf16, 64, 16><<<grid, block, 0, st>>>(a);
