@@ -1332,13 +1332,16 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
 
     // ---- merge the two key halves of each row half: waves kh = 1 hand (m, l, O) over
     float m_run = sm.m_ref, l_run = sm.l;
-    float *xo = (float *)smem;                                        // [rh][16*NT16][64] floats
+    // [rh][t16][g][lane] float4: each store and load moves 16 contiguous bytes per lane
+    float4 *xo = (float4 *)smem;
     float2 *xml = (float2 *)((char *)smem + 2 * 64 * 16 * NT16 * 4);  // [rh][64]
     if (kh == 1) {
 #pragma unroll
         for (int t16 = 0; t16 < NT16; t16++)
 #pragma unroll
-            for (int i = 0; i < 16; i++) xo[(rh * 16 * NT16 + t16 * 16 + i) * 64 + lane] = o[t16][i];
+            for (int g = 0; g < 4; g++)
+                xo[((rh * NT16 + t16) * 4 + g) * 64 + lane] =
+                    make_float4(o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2], o[t16][4 * g + 3]);
         xml[rh * 64 + lane] = make_float2(m_run, l_run);
     }
     __syncthreads();
@@ -1352,8 +1355,13 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int t16 = 0; t16 < NT16; t16++)
 #pragma unroll
-            for (int i = 0; i < 16; i++)
-                o[t16][i] = o[t16][i] * c0 + xo[(rh * 16 * NT16 + t16 * 16 + i) * 64 + lane] * c1;
+            for (int g = 0; g < 4; g++) {
+                const float4 x = xo[((rh * NT16 + t16) * 4 + g) * 64 + lane];
+                o[t16][4 * g] = o[t16][4 * g] * c0 + x.x * c1;
+                o[t16][4 * g + 1] = o[t16][4 * g + 1] * c0 + x.y * c1;
+                o[t16][4 * g + 2] = o[t16][4 * g + 2] * c0 + x.z * c1;
+                o[t16][4 * g + 3] = o[t16][4 * g + 3] * c0 + x.w * c1;
+            }
         m_run = M;
     }
 
