@@ -461,6 +461,162 @@ def run_tree_row(args):
     return line
 
 
+def guided_predictions(par, tok, rng, hit=0.85):
+    """Synthetic target predictions for a batch of trees: the target's greedy tokens follow a
+    random root-to-leaf walk (its first step always, each later one with probability `hit`),
+    anything else elsewhere; the verify kernels never see them, only the accept step does."""
+    B, N = par.shape
+    nxt = rng.integers(0, 1 << 20, size=(B, N)).astype(np.int32)
+    root = rng.integers(0, 1 << 20, size=B).astype(np.int32)
+    for b in range(B):
+        kids = {}
+        for j in range(N):
+            kids.setdefault(int(par[b, j]), []).append(j)
+        cur = -1
+        while kids.get(cur) and (cur < 0 or rng.random() < hit):
+            j = int(rng.choice(kids[cur]))
+            if cur < 0:
+                root[b] = tok[b, j]
+            else:
+                nxt[b, cur] = tok[b, j]
+            cur = j
+    return nxt, root
+
+
+def run_step_row(args):
+    """One whole speculative verify step on the GPU, stream-ordered with no host sync between
+    its stages: best-first tree build -> masks + plan -> attention -> combine -> greedy accept
+    -> KV compaction.  Checked once against the oracle chain, then K steps timed with
+    fence-free events between the stages."""
+    import dataclasses
+
+    import oracle
+    import tree_verify_mla_02_amd as kdt
+    from oracle import accept as oracle_accept
+    from oracle import tree_build as oracle_tree
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    inp = workloads.make_inputs(args.workload, seed=args.seed)
+    sp = inp.spec
+    B, N, H, dc = sp.batch, sp.nodes, sp.heads, sp.d_latent
+    D, K = (sp.depth, sp.topk) if sp.tree == "bestfirst" else (8, 8)
+    rng = np.random.default_rng([args.seed, 93])
+    lp = np.stack([workloads.drafter_logprobs(rng, D, K) for _ in range(B)]).astype(np.float32)
+    cand = rng.permutation(1 << 20)[: B * D * K].reshape(B, D, K).astype(np.int32)   # distinct token ids
+    par_ref, tok_ref, _, _ = oracle_tree.best_first_tree(lp, cand, N)
+    if (par_ref < -1).any():
+        raise SystemExit(f"depth {D} x top-{K} has fewer than {N} paths")
+    nxt, root = guided_predictions(par_ref, tok_ref, rng)
+    inp = dataclasses.replace(inp, parents=torch.from_numpy(par_ref.copy()))
+
+    d_lp, d_cand = torch.from_numpy(lp).to(dev), torch.from_numpy(cand).to(dev)
+    d_nxt, d_root = torch.from_numpy(nxt).to(dev), torch.from_numpy(root).to(dev)
+    lens = inp.cache_lens.to(dev)
+    q_lat, q_rope = inp.q_lat.to(dev), inp.q_rope.to(dev)
+    kv, tkv = inp.kv_cache.to(dev), inp.tree_kv.to(dev)
+    ckv, krope, tckv, tkrope = kv[:, :dc], kv[:, dc:], tkv[:, :, :dc], tkv[:, :, dc:]
+    maxL, T = int(inp.cache_lens.max()), inp.total_len
+    desc = kdt.make_desc(q_lat, q_rope, ckv, krope, tckv, tkrope, maxL, T)
+    ws = kdt.alloc_workspace(desc, dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    parents, tokens, depth, rank = (torch.empty((B, N), **i32) for _ in range(4))
+    masks = torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device=dev)
+    out = torch.empty((B, N, H, dc), dtype=torch.float32, device=dev)
+    path, acc, bonus, new_lens = torch.empty((B, N), **i32), torch.empty(B, **i32), torch.empty(B, **i32), \
+        torch.empty(B, **i32)
+    cap = T + B * N
+    kv_out = torch.empty((cap, kv.shape[1]), dtype=kv.dtype, device=dev)
+    status = torch.zeros(1, **i32)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(rec=None):
+        mark = (lambda k: rec(k)) if rec else (lambda k: None)
+        mark(0)
+        kdt.build_tree(d_lp, d_cand, N, parents, tokens, depth, rank, stream=stream)
+        mark(1)
+        kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
+        mark(2)
+        kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
+        mark(3)
+        kdt.combine(out, desc, ws, stream=stream)
+        mark(4)
+        kdt.tree_accept(parents, tokens, d_nxt, d_root, path, acc, bonus, stream=stream)
+        mark(5)
+        kdt.kv_compact(ckv, krope, lens, tckv, tkrope, path, acc, desc, kv_out[:, :dc], kv_out[:, dc:],
+                       new_lens=new_lens, capacity_rows=cap, dev_status=status, stream=stream)
+        mark(6)
+
+    step()
+    torch.cuda.synchronize()
+    # ---- the chain against the oracle chain: integer stages bit for bit, attention sampled rows
+    if int(status.item()) != 0:
+        raise SystemExit(f"device status {int(status.item())} on the benchmark inputs")
+    if not (np.array_equal(parents.cpu().numpy(), par_ref) and np.array_equal(tokens.cpu().numpy(), tok_ref)):
+        raise SystemExit("tree differs from the oracle")
+    ref_masks, _ = oracle.visibility(par_ref)
+    if not np.array_equal(masks.cpu().numpy().view(np.uint64), ref_masks):
+        raise SystemExit("masks differ from the oracle")
+    R = N * H
+    rows = np.unique(np.concatenate([b * R + np.array([0, R - 1]) for b in range(B)] +
+                                    [rng.integers(0, B * R, size=64)]))
+    ref_out = oracle.run(inp, rows=rows)[1].reshape(-1, dc)
+    err = float(np.abs(out.reshape(-1, dc)[torch.from_numpy(rows).to(dev)].cpu().double().numpy() - ref_out).max())
+    tol = 2e-3 if sp.dtype == "bf16" else 1e-5
+    if err > tol:
+        raise SystemExit(f"attention max-abs error {err} above {tol}")
+    w_path, w_acc, w_bonus = oracle_accept.tree_accept(par_ref, tok_ref, nxt, root)
+    if not (np.array_equal(path.cpu().numpy(), w_path) and np.array_equal(acc.cpu().numpy(), w_acc)
+            and np.array_equal(bonus.cpu().numpy(), w_bonus)):
+        raise SystemExit("accept differs from the oracle")
+    as_i16 = (lambda t: t.view(torch.int16).numpy()) if sp.dtype == "bf16" else (lambda t: t.view(torch.int32).numpy())
+    wc, wr, wl = oracle_accept.kv_compact(as_i16(inp.kv_cache[:, :dc]), as_i16(inp.kv_cache[:, dc:]),
+                                          inp.cache_lens.numpy().astype(np.int64), as_i16(inp.tree_kv[:, :, :dc]),
+                                          as_i16(inp.tree_kv[:, :, dc:]), w_path.astype(np.int64),
+                                          w_acc.astype(np.int64))
+    n_new = int(wl.sum())
+    got = kv_out[:n_new].cpu()
+    if not (np.array_equal(as_i16(got[:, :dc]), wc) and np.array_equal(as_i16(got[:, dc:]), wr)
+            and np.array_equal(new_lens.cpu().numpy(), wl)):
+        raise SystemExit("compaction differs from the oracle")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    he = HipEvents()
+    evs = [[he.create() for _ in range(7)] for _ in range(args.steps)]
+    ev0, ev1 = he.create(), he.create()
+    he.record(ev0, stream)
+    for i in range(args.steps):
+        step(lambda k, i=i: he.record(evs[i][k], stream))
+    he.record(ev1, stream)
+    torch.cuda.synchronize()
+    step_ms = he.elapsed_ms(ev0, ev1) / args.steps
+    names = ["tree_build", "prepare", "attend", "combine", "accept", "compact"]
+    stage = {n: float(np.mean([he.elapsed_ms(e[k], e[k + 1]) for e in evs])) for k, n in enumerate(names)}
+    he.close()
+    flops, nbytes, cache_bytes = algorithmic_work(inp)
+    mfma_peak = PEAK_BF16_TFLOPS if sp.dtype == "bf16" else PEAK_F32_TFLOPS
+    if flops / nbytes < mfma_peak * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        bound, peak, unit_r, achieved = "hbm", PEAK_HBM_GBPS, "GB/s", nbytes / (stage["attend"] * 1e-3) / 1e9
+    else:
+        bound, peak, unit_r, achieved = "mfma", mfma_peak, "TFLOP/s", flops / (stage["attend"] * 1e-3) / 1e12
+    line = {
+        "metric": "DDTree verify step (tree build, masks + plan, attention, combine, accept, compaction) requests/s",
+        "value": round(B / (step_ms * 1e-3), 3), "unit": "requests/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": sp.dtype,
+        "data": "synthetic (seeded drafter log probabilities, N(0,1) queries and cache, guided target predictions)",
+        "config": {"workload": f"step on {sp.name}: B={B} requests, N={N} nodes (depth<={D}, top-{K}), H={H} heads, "
+                               f"cache={maxL} tokens, {sp.dtype}", "batch": B, "nodes": N, "heads": H,
+                   "cache_len": maxL, "splits": kdt.num_splits(desc)},
+        "stage_us": {n: round(v * 1e3, 2) for n, v in stage.items()},
+        "accepted_tokens": int(w_acc.sum()), "attention_max_abs_err_sampled": err,
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit_r,
+                     "frac": round(achieved / peak, 4), "traffic": None},
+    }
+    return line
+
+
 # HBM traffic of the attention kernel per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # summarised under profiles/.  The summary records a hash of the kernel sources it was taken
 # on; when the sources have changed since, the figure no longer describes this kernel and
@@ -514,10 +670,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="attention launches timed after flushing L2 and MALL (0 to skip)")
-    ap.add_argument("--row", default="verify", choices=["verify", "accept", "compact", "tree"],
+    ap.add_argument("--row", default="verify", choices=["verify", "accept", "compact", "tree", "step"],
                     help="verify: the tree-verify attention step (default); accept / compact / tree: the greedy "
                          "tree-accept, the KV compaction or the best-first tree builder kernel alone, on the "
-                         "workload's trees and lengths")
+                         "workload's trees and lengths; step: a whole verify step, all of them chained")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -536,6 +692,9 @@ def main():
         return
     if args.row == "tree":
         print(json.dumps(run_tree_row(args)), flush=True)
+        return
+    if args.row == "step":
+        print(json.dumps(run_step_row(args)), flush=True)
         return
     if args.row != "verify":
         print(json.dumps(run_next_row(args)), flush=True)
