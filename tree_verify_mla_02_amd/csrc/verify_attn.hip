@@ -1576,10 +1576,11 @@ hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st) {
     const int64_t tiles = (int64_t)a.B * ((a.R + kRowsPerWave - 1) / kRowsPerWave) * (d_latent / 32);
     // Waves per tile: first more waves share a tile (each keeping at least 4 splits), then a
     // tile's four column groups go to 2 or 4 waves, while the grid stays within about 8 waves
-    // per CU (2048 on 256 CUs).  Measured best on the split counts 8, 16, 32 and 128 (the
-    // Kimi, 7-node, 16-node and decode shapes): 1 x 4, 4 x 2, 4 x 4 and 8 x 1 waves x groups.
+    // per CU (2048 on 256 CUs).  Measured best on the split counts 8, 16 and 32 (the Kimi,
+    // 7-node and 16-node shapes): 1 x 4, 4 x 2 and 4 x 4 waves x groups; decode (128 splits,
+    // 32 tiles) takes 16 x 1, 1.2 us faster than 8 x 1.
     int ws = 1, gc = 4;
-    while (ws < 8 && tiles * ws * 2 <= 2048 && ws * 2 * 4 <= a.S) ws *= 2;
+    while (ws < 16 && tiles * ws * 2 <= 2048 && ws * 2 * 4 <= a.S) ws *= 2;
     while (gc > 1 && tiles * ws * (4 / gc) * 2 <= 2048) gc /= 2;
     const int64_t subs = tiles * (4 / gc);
     const int nw = ws > kWaves ? ws : kWaves;
@@ -1589,6 +1590,7 @@ hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st) {
     auto go = [&](auto dc, auto gcv) {
         constexpr int DCv = decltype(dc)::value, GC = decltype(gcv)::value;
         switch (ws) {
+            case 16: combine_kernel<DCv, 16, GC><<<grid, block, 0, st>>>(a); break;
             case 8: combine_kernel<DCv, 8, GC><<<grid, block, 0, st>>>(a); break;
             case 4: combine_kernel<DCv, 4, GC><<<grid, block, 0, st>>>(a); break;
             case 2: combine_kernel<DCv, 2, GC><<<grid, block, 0, st>>>(a); break;
