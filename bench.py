@@ -513,9 +513,15 @@ def run_step_row(args):
     d_nxt, d_root = torch.from_numpy(nxt).to(dev), torch.from_numpy(root).to(dev)
     lens = inp.cache_lens.to(dev)
     q_lat, q_rope = inp.q_lat.to(dev), inp.q_rope.to(dev)
-    kv, tkv = inp.kv_cache.to(dev), inp.tree_kv.to(dev)
-    ckv, krope, tckv, tkrope = kv[:, :dc], kv[:, dc:], tkv[:, :, :dc], tkv[:, :, dc:]
     maxL, T = int(inp.cache_lens.max()), inp.total_len
+    # the cache buffer has room for N more rows per request; one request compacts in place
+    # (only its accepted rows move), a batch into a second buffer
+    in_place = B == 1
+    cap = T + B * N
+    kv = torch.empty((cap, inp.kv_cache.shape[1]), dtype=inp.kv_cache.dtype, device=dev)
+    kv[:T] = inp.kv_cache.to(dev)
+    tkv = inp.tree_kv.to(dev)
+    ckv, krope, tckv, tkrope = kv[:, :dc], kv[:, dc:], tkv[:, :, :dc], tkv[:, :, dc:]
     desc = kdt.make_desc(q_lat, q_rope, ckv, krope, tckv, tkrope, maxL, T)
     ws = kdt.alloc_workspace(desc, dev)
     i32 = dict(dtype=torch.int32, device=dev)
@@ -524,8 +530,7 @@ def run_step_row(args):
     out = torch.empty((B, N, H, dc), dtype=torch.float32, device=dev)
     path, acc, bonus, new_lens = torch.empty((B, N), **i32), torch.empty(B, **i32), torch.empty(B, **i32), \
         torch.empty(B, **i32)
-    cap = T + B * N
-    kv_out = torch.empty((cap, kv.shape[1]), dtype=kv.dtype, device=dev)
+    kv_out = kv if in_place else torch.empty((cap, kv.shape[1]), dtype=kv.dtype, device=dev)
     status = torch.zeros(1, **i32)
     stream = torch.cuda.current_stream(dev)
 
@@ -608,7 +613,8 @@ def run_step_row(args):
         "data": "synthetic (seeded drafter log probabilities, N(0,1) queries and cache, guided target predictions)",
         "config": {"workload": f"step on {sp.name}: B={B} requests, N={N} nodes (depth<={D}, top-{K}), H={H} heads, "
                                f"cache={maxL} tokens, {sp.dtype}", "batch": B, "nodes": N, "heads": H,
-                   "cache_len": maxL, "splits": kdt.num_splits(desc)},
+                   "cache_len": maxL, "splits": kdt.num_splits(desc),
+                   "compaction": "in place" if in_place else "into a second buffer"},
         "stage_us": {n: round(v * 1e3, 2) for n, v in stage.items()},
         "accepted_tokens": int(w_acc.sum()), "attention_max_abs_err_sampled": err,
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit_r,
