@@ -620,6 +620,41 @@ def run_step_row(args):
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit_r,
                      "frac": round(achieved / peak, 4), "traffic": None},
     }
+    if not getattr(args, "no_cpu_baseline", True):
+        # the oracle chain on the host cores: tree, masks + attention rows, accept, compaction.
+        # Steps above ~40 GFLOP run the attention on a random sample of rows and scale it to
+        # every row (the oracle's cost is linear in the rows).
+        cores = len(os.sched_getaffinity(0))
+        oracle.build()
+        total_rows = B * R
+        sample = total_rows if flops <= 40e9 else max(64, int(total_rows * 40e9 / flops))
+        srows = None if sample == total_rows else np.sort(rng.choice(total_rows, size=sample, replace=False))
+        reps, t_attn, t_rest = 0, 0.0, 0.0
+        t0 = time.perf_counter()
+        while True:
+            a = time.perf_counter()
+            p_ref = oracle_tree.best_first_tree(lp, cand, N)[0]
+            b_ = time.perf_counter()
+            oracle.run(dataclasses.replace(inp, parents=torch.from_numpy(p_ref)), rows=srows, threads=cores)
+            c = time.perf_counter()
+            a_path, a_acc, _ = oracle_accept.tree_accept(p_ref, tok_ref, nxt, root)
+            oracle_accept.kv_compact(as_i16(inp.kv_cache[:, :dc]), as_i16(inp.kv_cache[:, dc:]),
+                                     inp.cache_lens.numpy().astype(np.int64), as_i16(inp.tree_kv[:, :, :dc]),
+                                     as_i16(inp.tree_kv[:, :, dc:]), a_path.astype(np.int64), a_acc.astype(np.int64))
+            d_ = time.perf_counter()
+            t_attn += c - b_
+            t_rest += (b_ - a) + (d_ - c)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 10.0 or dt * (reps + 1) / reps > 30.0:
+                break
+        step_s = (t_rest + t_attn * total_rows / sample) / reps
+        line["cpu_baseline"] = {
+            "value": round(B / step_s, 3), "unit": "requests/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} step(s) of the same workload in {dt:.2f} s: tree, masks, "
+                      + (f"all {total_rows} attention rows" if srows is None else
+                         f"{sample} of {total_rows} attention rows (scaled to all)")
+                      + f" in fp64 on {cores} threads, accept, compaction"}
     return line
 
 
