@@ -131,7 +131,8 @@ kdt::AttnArgs make_args(const kdt_verify_desc &d, const kdt::Geometry &g, void *
     a.H = d.num_heads;
     a.W = g.mask_words;
     a.R = g.rows;
-    a.RT = g.row_tiles;
+    a.RT = g.layout_tiles;
+    a.tile_rows = g.tile_rows;
     a.S = g.nsplit;
     a.chunk = g.chunk;
     a.hdr = (const kdt::WsHeader *)(w + g.off_header);
@@ -150,9 +151,17 @@ namespace kdt {
 bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     Geometry x{};
     x.rows = (int64_t)d.num_nodes * d.num_heads;
-    const int64_t rt = (x.rows + kRowsPerTile - 1) / kRowsPerTile;
+    // Requests of at most 512 rows (a decode step, small trees) take 64-row workgroups when
+    // 128-row ones would not fill the GPU: twice the workgroups for the same keys, each wave
+    // working on one 32-key block of every tile (bf16, d = 512 + 64 only).
+    const int64_t rt128 = (x.rows + kRowsPerTile - 1) / kRowsPerTile;
+    const bool small = d.dtype == KDT_BF16 && d.d_latent == 512 && d.d_rope == 64 && x.rows <= 512 &&
+                       (int64_t)d.batch * rt128 < num_cus;
+    x.tile_rows = small ? kRowsPerTile / 2 : kRowsPerTile;
+    const int64_t rt = (x.rows + x.tile_rows - 1) / x.tile_rows;
     if (rt > (1 << 30)) return false;
     x.row_tiles = (int)rt;
+    x.layout_tiles = (int)rt128;
     x.mask_words = (d.num_nodes + 63) / 64;
     const int64_t units0 = (int64_t)d.batch * rt;
     const int64_t maxL = d.max_cache_len;
@@ -201,7 +210,7 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     x.off_units = take(sizeof(kdt::Unit) * (size_t)x.units);
     if (S > 1) {
         x.off_ml = take(8 * (size_t)B * S * x.rows);
-        x.off_o = take(3 * (size_t)B * S * rt * kRowsPerTile * d.d_latent);   // whole row tiles, 24-bit
+        x.off_o = take(3 * (size_t)B * S * rt128 * kRowsPerTile * d.d_latent);   // whole 128-row tiles, 24-bit
     } else {
         x.off_ml = x.off_o = 0;
     }

@@ -28,7 +28,9 @@ constexpr int kMaxTreeTable = 8192;                    // tree builder: D * K lo
 
 struct Geometry {
     int64_t rows;          // R = N * H query rows per request
-    int row_tiles;         // RT = ceil(R / 128)
+    int tile_rows;         // query rows per workgroup: 128, or 64 for small requests (see make_geometry)
+    int row_tiles;         // RT = ceil(R / tile_rows): row tiles of the unit list
+    int layout_tiles;      // ceil(R / 128): 128-row tiles of the split-partial layout
     int nsplit;            // S: splits per request at most (1 = no split)
     int64_t chunk;         // committed keys per split
     int64_t units;         // grid size of the attention kernel: 8 * ceil(G / 8) * bt * bs slots
@@ -65,7 +67,8 @@ struct AttnArgs {
     int64_t q_lat_stride, q_rope_stride, ckv_stride, krope_stride, tckv_stride, tkrope_stride;
     int B, N, H, W;
     int64_t R;
-    int RT, S;
+    int RT, S;             // RT: 128-row tiles of the partial layout
+    int tile_rows;         // 128: verify_attn_kernel; 64: the 64-row kernel (unit rt counts 64-row tiles)
     int64_t chunk;
     float scale_log2;      // scale * log2(e): scores are kept in the base-2 domain
     const WsHeader *hdr;

@@ -1196,14 +1196,18 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
 
     const Unit unit = a.units[blockIdx.x];
     if (unit.b < 0) return;
-    const int b = unit.b, s = unit.s, sb = unit.sb;     // one row tile: unit.rt == 0
+    const int b = unit.b, s = unit.s, sb = unit.sb;
+    // 64-row tile of the unit: unit.rt counts 64-row tiles when the plan was made for them, and
+    // is 0 for a request of at most 64 rows under 128-row tiles
+    const int rt64 = a.tile_rows == 2 * kRowsPerWave ? unit.rt : 0;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rh = wave & 1, kh = wave >> 1;            // row half, key half
     const int half = lane >> 5;
-    const int64_t R = a.R;                              // <= 64 (checked by the launcher)
+    const int64_t R = a.R;
+    const int64_t row0 = (int64_t)rt64 * 2 * kRowsPerWave;          // the workgroup's first row
 
-    const int64_t r = (int64_t)rh * kRowsPerWave + (lane & 31);
+    const int64_t r = row0 + (int64_t)rh * kRowsPerWave + (lane & 31);
     const bool row_ok = r < R;
     const int64_t rc = row_ok ? r : R - 1;
     const int node = (int)(rc / a.H);
@@ -1235,12 +1239,13 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
         dma_setup(d0, 0, 0);
         d0.template issue<0, Dma::NINST>();
     }
-    // the request's rows (at most 64) go to buffer 1 together with tile 0: one round trip
+    // the workgroup's rows (at most 64) go to buffer 1 together with tile 0: one round trip
     LDS_AS char *qbuf = (LDS_AS char *)smem + Sh::TILE_BYTES;
     {
+        const int64_t nrows = R - row0 < 2 * kRowsPerWave ? R - row0 : 2 * kRowsPerWave;
         Dma dq;
-        dq.setup(qbuf, (const T *)a.q_lat, a.q_lat_stride, (const T *)a.q_rope, a.q_rope_stride, (int64_t)b * R,
-                 (int)R, wave, lane);
+        dq.setup(qbuf, (const T *)a.q_lat, a.q_lat_stride, (const T *)a.q_rope, a.q_rope_stride,
+                 (int64_t)b * R + row0, (int)nrows, wave, lane);
         dq.template issue<0, Dma::NINST>();
     }
 
@@ -1381,7 +1386,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
             }
     } else {
         const int64_t prow = ((int64_t)b * a.S + s) * R + r;
-        const int64_t blk = (((int64_t)b * a.S + s) * a.RT + 0) * kWaves + rh;
+        // 32-row group 2*rt64 + rh of the request = group (rt64 & 1)*2 + rh of 128-row tile rt64/2
+        const int64_t blk = (((int64_t)b * a.S + s) * a.RT + (rt64 >> 1)) * kWaves + (rt64 & 1) * 2 + rh;
         uint32_t *dst = a.part_o + blk * (kRowsPerWave * DC / 4 * 3) + lane * 3;
 #pragma unroll
         for (int t16 = 0; t16 < NT16; t16++)
@@ -1559,7 +1565,10 @@ hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t
 
 hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units, hipStream_t st) {
     const dim3 grid((unsigned)units), block(256);
-    if (dtype == KDT_BF16 && d_latent == 512 && d_rope == 64 && a.R <= 2 * kRowsPerWave)
+    if (a.tile_rows == 2 * kRowsPerWave) {
+        if (dtype != KDT_BF16 || d_latent != 512 || d_rope != 64) return hipErrorInvalidValue;
+        decode_attn_kernel<512, 64><<<grid, block, 0, st>>>(a);
+    } else if (dtype == KDT_BF16 && d_latent == 512 && d_rope == 64 && a.R <= 2 * kRowsPerWave)
         decode_attn_kernel<512, 64><<<grid, block, 0, st>>>(a);
     else if (dtype == KDT_BF16 && d_latent == 512 && d_rope == 64)
         verify_attn_kernel<__bf16, 512, 64><<<grid, block, 0, st>>>(a);
