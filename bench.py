@@ -269,20 +269,7 @@ def accept_inputs(inp, seed):
     B, N = par.shape
     rng = np.random.default_rng([seed, 77])
     tok = rng.permutation(B * N * 4)[: B * N].reshape(B, N).astype(np.int32)
-    nxt = rng.integers(0, 1 << 20, size=(B, N)).astype(np.int32)
-    root = rng.integers(0, 1 << 20, size=B).astype(np.int32)
-    for b in range(B):
-        kids = {}
-        for j in range(N):
-            kids.setdefault(int(par[b, j]), []).append(j)
-        cur = -1
-        while kids.get(cur) and (cur < 0 or rng.random() < 0.85):
-            j = int(rng.choice(kids[cur]))
-            if cur < 0:
-                root[b] = tok[b, j]
-            else:
-                nxt[b, cur] = tok[b, j]
-            cur = j
+    nxt, root = guided_predictions(par, tok, rng)
     return par.astype(np.int32), tok, nxt, root
 
 
@@ -672,12 +659,19 @@ KERNEL_SOURCES = {
 
 
 def kernel_source_hash(kernel: str = "verify_attn") -> str:
+    """Hash of the code a kernel is compiled from: its sources with comments, blank lines and
+    trailing blanks removed, so that an edit of a comment leaves it unchanged."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_verify_mla_02_amd", "csrc")
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(name.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, name)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        code = "\n".join(ln for ln in lines if ln.strip())
+        h.update(name.encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
 
 

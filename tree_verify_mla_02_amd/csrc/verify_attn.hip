@@ -1104,17 +1104,18 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     }
 }
 
-// ------------------------------------------------------------------------------ decode shape
-// Requests of at most 64 query rows (a decode step: one node x up to 64 heads).  With the
-// 128-row workgroup above half of the rows would be empty, and every wave would still issue
-// the 200 MFMAs of a 64-key tile: one CU's matrix pipes, not HBM, would bound the key stream.
-// Here a workgroup takes the request's 64 rows and wave w = (key half kh, row half rh) takes
-// rows 32*rh .. +31 and keys 32*kh .. +31 of every tile: 36 QK + 64 P.V MFMAs per tile and wave
-// instead of 72 + 128, so a tile costs each SIMD about half the time.  Each wave keeps its own
-// online softmax (m, l, O) over its key half; at the end the two key halves of a row half are
-// merged through LDS, and the merged wave writes the output or the split partial exactly as the
-// 128-row kernel's wave rh would (the combine is shared).  Same unit records, tile copies, LDS
-// layout, fragment patterns and precision (P as bf16 hi + lo) as the 128-row kernel.
+// ------------------------------------------------------------------------------ 64-row workgroups
+// Small requests: a decode step (one node x up to 64 heads) or a small tree, at most 512 rows.
+// With the 128-row workgroup above a 64-row request would leave half of the rows empty, and
+// every wave would still issue the 200 MFMAs of a 64-key tile: one CU's matrix pipes, not HBM,
+// would bound the key stream.  Here a workgroup takes 64 rows and wave w = (key half kh, row
+// half rh) takes rows 32*rh .. +31 and keys 32*kh .. +31 of every tile: 36 QK + 64 P.V MFMAs
+// per tile and wave instead of 72 + 128, and twice the workgroups for a small tree.  Each wave
+// keeps its own online softmax (m, l, O) over its key half; at the end the two key halves of a
+// row half are merged through LDS, and the merged wave writes the output or the split partial
+// exactly as the 128-row kernel's wave would (the partial layout stays in 128-row tiles and the
+// combine is shared).  Same unit records, tile copies, LDS layout, fragment patterns and
+// precision (P as bf16 hi + lo) as the 128-row kernel.
 
 // S^T of one 32-key block x this wave's 32 rows: a chain of NQ MFMA 32x32x16 on one
 // accumulator, K fragments read QD steps ahead (pq already points at the wave's block).
