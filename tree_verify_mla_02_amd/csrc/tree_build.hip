@@ -20,8 +20,8 @@
 // child).  Slot j = p + 1 lives in lane j % 64, register slot j / 64 (at most 5 per lane for
 // N <= 256).  Equal scores go to the earlier push; an entry's push number is counted exactly
 // as a heap would count it (a next sibling is pushed before the first child).  A pop is a wave
-// max over the 64 lane bests (DPP inside rows of 16 lanes, lane reads across rows) and a
-// ballot for the lane that holds it; the winner's fields come back by lane reads, and one LDS
+// max over the 64 lane bests (DPP inside rows of 16 lanes and row broadcasts across them) and
+// a ballot for the lane that holds it; the winner's fields come back by lane reads, and one LDS
 // read of the log-probability table gives the two new entry scores.  The order key is the
 // score's fp32 pattern mapped to an unsigned integer that sorts like the float (zeroes of
 // either sign map to one key).
@@ -34,6 +34,21 @@ __device__ __forceinline__ uint32_t order_key(float v) {
     if (v == 0.0f) v = 0.0f;
     const uint32_t u = __float_as_uint(v);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Max over a wave of 64: within each row of 16 lanes by DPP (quad swaps, row rotations by 4
+// and 8), then row 0 into row 1 and row 2 into row 3 (row_bcast:15), then rows 0-1 into rows
+// 2-3 (row_bcast:31); lane 63 then holds the maximum.  Uniform result.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));   // row_ror 4
+    v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));   // row_ror 8
+    // rows that receive no broadcast keep their value (old = v, bound_ctrl off)
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));   // row_bcast:15
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Reductions over a wave of 64: within each row of 16 lanes by DPP (quad swaps, then row
@@ -100,7 +115,7 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const float *__restrict_
 
     int n = 0;
     for (; n < N; n++) {
-        const uint32_t top = wave_reduce_u32<true>(best_key);
+        const uint32_t top = wave_max_u32(best_key);
         if (top == 0u) break;                                       // the frontier is empty
         // the lane holding the best entry; only equal best scores in several lanes (rare)
         // need the push numbers compared
@@ -150,8 +165,8 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const float *__restrict_
                 dr[i] = (uint32_t)(d + 1) << 16;
             }
         });
-        if (lane == jl || lane == jnl) {                            // rescan the changed lanes
-            best_key = 0u;
+        {                                   // rescan (only lanes jl and jnl changed; the others
+            best_key = 0u;                  // recompute the same best, with no branch)
             best_tie = 0u;
             best_slot = 0;
             each_slot<0, S>([&](auto I) {
