@@ -1566,12 +1566,15 @@ hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t
 
 hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units, hipStream_t st) {
     const dim3 grid((unsigned)units), block(256);
+    const bool kimi_dims = dtype == KDT_BF16 && d_latent == 512 && d_rope == 64;
+    // 64-row workgroups: the plan made 64-row tiles, or (128-row tiles of a batch that fills the
+    // GPU) a request has at most 64 rows, its one tile at rt = 0
     if (a.tile_rows == 2 * kRowsPerWave) {
-        if (dtype != KDT_BF16 || d_latent != 512 || d_rope != 64) return hipErrorInvalidValue;
+        if (!kimi_dims) return hipErrorInvalidValue;
         decode_attn_kernel<512, 64><<<grid, block, 0, st>>>(a);
-    } else if (dtype == KDT_BF16 && d_latent == 512 && d_rope == 64 && a.R <= 2 * kRowsPerWave)
+    } else if (kimi_dims && a.R <= 2 * kRowsPerWave)
         decode_attn_kernel<512, 64><<<grid, block, 0, st>>>(a);
-    else if (dtype == KDT_BF16 && d_latent == 512 && d_rope == 64)
+    else if (kimi_dims)
         verify_attn_kernel<__bf16, 512, 64><<<grid, block, 0, st>>>(a);
     else if (dtype == KDT_BF16 && d_latent == 64 && d_rope == 16)
         verify_attn_kernel<__bf16, 64, 16><<<grid, block, 0, st>>>(a);
