@@ -240,3 +240,21 @@ def test_abi_errors_on_device():
         kdt.build_visibility(torch.zeros((1, 257), dtype=torch.int32, device="cuda"))
     assert e.value.code == kdt._lib.KDT_ERR_UNSUPPORTED
     print("PASS ABI error paths", flush=True)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_small_requests(seed):
+    """Random small batches (at most 512 rows per request, so they take 64-row workgroups when the
+    batch is small, 128-row ones otherwise): random trees, heads, ragged lengths with empty
+    caches and one-key tails, all rows against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    for case in range(4):
+        B = int(rng.integers(1, 7))
+        H = int(rng.choice([1, 3, 8, 16, 64]))
+        N = int(rng.integers(1, max(2, min(256, 512 // H)) + 1))
+        lo = int(rng.integers(0, 2))
+        hi = int(rng.integers(lo, 2500))
+        spec = workloads.Spec(f"rnd{seed}_{case}", 90 + seed, B, N, H, 512, 64, "bf16", None, ragged=(lo, hi),
+                              tree="random", outlier_p=0.01 if case == 3 else 0.0)
+        inp = workloads.make_inputs(spec, seed=case)
+        check(f"random small request seed {seed} case {case}", inp)
