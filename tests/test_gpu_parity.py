@@ -90,6 +90,11 @@ SMALL = {
                      None),
     "dec_unsplit": (workloads.Spec("dec_u", 64, 600, 1, 64, 512, 64, "bf16", None, ragged=(1, 200), tree="chain"),
                     None),
+    # small requests in a batch that fills the GPU: 128-row workgroups, no split
+    "batch300": (workloads.Spec("b300", 65, 300, 2, 64, 512, 64, "bf16", None, ragged=(1, 300), tree="random"), None),
+    # 1000 rows: 128-row workgroups with a partial last tile, two mask words, a split
+    "rows1000": (workloads.Spec("r1000", 66, 2, 125, 8, 512, 64, "bf16", None, ragged=(700, 2600), depth=10, topk=6),
+                 None),
 }
 
 
