@@ -17,8 +17,9 @@
 // therefore kept as one slot per prefix p (p = -1 for depth 1, else a popped node), holding
 // that child's rank r, the prefix's score and the entry's score; a pop moves the slot of the
 // popped child's prefix on to rank r + 1 and opens the slot of the new node (its rank-0
-// child).  Slot j = p + 1 lives in lane j % 64, register slot j / 64 (at most 5 per lane for
-// N <= 256).  Equal scores go to the earlier push; an entry's push number is counted exactly
+// child).  Slot j = p + 1 lives in lane j % 64, register slot j / 64; the last node opens no
+// slot (nothing is popped after it), so slots 0 .. N-1 suffice: at most 4 per lane for
+// N <= 256.  Equal scores go to the earlier push; an entry's push number is counted exactly
 // as a heap would count it (a next sibling is pushed before the first child).  A pop is a wave
 // max over the 64 lane bests (DPP inside rows of 16 lanes and row broadcasts across them) and
 // a ballot for the lane that holds it; the winner's fields come back by lane reads, and one LDS
@@ -84,7 +85,7 @@ __device__ __forceinline__ uint32_t fetch(const uint32_t (&v)[S], int slot, int 
     return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
 }
 
-// S = register slots per lane: ceil((N + 1) / 64).
+// S = register slots per lane: ceil(N / 64).
 template <int S>
 __global__ __launch_bounds__(64) void tree_build_kernel(const float *__restrict__ logp,
                                                         const int32_t *__restrict__ cand, int D, int K,
@@ -147,8 +148,9 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const float *__restrict_
         const float e_child = score + lp_child;
         const uint32_t k_sib = sib ? order_key(e_sib) : 0u;
         const uint32_t k_child = child ? order_key(e_child) : 0u;
-        // slot j moves on to rank r + 1; slot n + 1 opens with the new node's rank-0 child
-        const int jn = n + 1, jnl = jn & 63, jns = jn >> 6;
+        // slot j moves on to rank r + 1; slot n + 1 opens with the new node's rank-0 child (not
+        // for the last node: nothing is popped after it, so slots 0 .. N-1 suffice)
+        const int jn = n + 1 < N ? n + 1 : -1, jnl = jn & 63, jns = jn < 0 ? -1 : jn >> 6;
         each_slot<0, S>([&](auto I) {
             constexpr int i = I.value;
             if (lane == jl && i == js) {
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(64) void tree_build_kernel(const float *__restrict_
 hipError_t launch_tree_build(const float *logp, const int32_t *cand, int B, int D, int K, int N,
                              int32_t *parents, int32_t *tokens, int32_t *depth, int32_t *rank, hipStream_t st) {
     const size_t lds = (size_t)D * K * sizeof(float);
-    const int slots = (N + 1 + 63) / 64;
+    const int slots = (N + 63) / 64;
     auto go = [&](auto kernel) {
         kernel<<<(unsigned)B, 64, lds, st>>>(logp, cand, D, K, N, parents, tokens, depth, rank);
     };
@@ -209,7 +211,6 @@ hipError_t launch_tree_build(const float *logp, const int32_t *cand, int B, int 
         case 2: go(tree_build_kernel<2>); break;
         case 3: go(tree_build_kernel<3>); break;
         case 4: go(tree_build_kernel<4>); break;
-        case 5: go(tree_build_kernel<5>); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
