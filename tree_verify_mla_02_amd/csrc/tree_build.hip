@@ -42,13 +42,14 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 // 2-3 (row_bcast:31); lane 63 then holds the maximum.  Uniform result.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
-    v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
-    v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
-    v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false));   // row_ror 4
-    v = mx(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));   // row_ror 8
-    // rows that receive no broadcast keep their value (old = v, bound_ctrl off)
-    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));   // row_bcast:15
-    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));   // row_bcast:31
+    // lanes a move does not write read 0, the identity of an unsigned max, so each move can
+    // fold into the max instruction
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));    // quad_perm 1,0,3,2
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));    // quad_perm 2,3,0,1
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, true));   // row_ror 4
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, true));   // row_ror 8
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, true));   // row_bcast:15
+    v = mx(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, true));   // row_bcast:31
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
