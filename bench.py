@@ -139,11 +139,15 @@ def run(args):
         kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
         kdt.combine(out, desc, ws, stream=stream)
 
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise SystemExit(f"device status {int(status.item())} on the benchmark inputs")
+    # the outputs of the warm-up steps against the oracle before anything is timed: masks bit
+    # for bit, attention rows within the tolerance (every row up to ~40 GFLOP of oracle work,
+    # else one row of every 32-row group of every request plus random rows)
+    check = check_outputs(inp, masks, out)
 
     # ---- timed region: K whole steps; the attention kernel's own launches are bracketed by
     # events on the stream it runs on (the same stream as the rest of the step)
@@ -171,21 +175,25 @@ def run(args):
     attn_each = np.array([he.elapsed_ms(a, b) for a, b in evs])
     attn_ms = float(attn_each.mean())
 
-    # ---- cold caches: before each of a few attention launches, write a 512 MiB scratch buffer
-    # (twice the 256 MB Infinity Cache) so the launch starts with cold L2 and MALL
-    cold = []
+    # ---- cold caches: before each of a few steps, write a 512 MiB scratch buffer (twice the
+    # 256 MB Infinity Cache) so the step starts with cold L2 and MALL; the attention launch and
+    # the whole step are timed
+    cold, cold_step = [], []
     if args.cold_steps:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         for _ in range(args.cold_steps):
             scratch.fill_(1)
+            s0, a0, a1, s1 = he.create(), he.create(), he.create(), he.create()
+            he.record(s0, stream)
             kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
-            a0, a1 = he.create(), he.create()
             he.record(a0, stream)
             kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
             he.record(a1, stream)
             kdt.combine(out, desc, ws, stream=stream)
+            he.record(s1, stream)
             torch.cuda.synchronize()
             cold.append(he.elapsed_ms(a0, a1))
+            cold_step.append(he.elapsed_ms(s0, s1))
         del scratch
     he.close()
 
@@ -199,6 +207,15 @@ def run(args):
     else:
         bound, peak, unit_r = "mfma", mfma_peak, "TFLOP/s"
         achieved = flops / (attn_ms * 1e-3) / 1e12
+
+    def frac(ms):
+        """Fraction of the binding roof reached by a region of `ms` milliseconds."""
+        if ms is None:
+            return None
+        rate = nbytes / (ms * 1e-3) / 1e9 if hbm_bound else flops / (ms * 1e-3) / 1e12
+        return round(rate / peak, 4)
+    cold_ms = float(np.median(cold)) if cold else None
+    cold_step_ms = float(np.median(cold_step)) if cold_step else None
     value = flops / (step_ms * 1e-3) / 1e12
     line = {
         "metric": "tree-verify attn TFLOP/s + cache GB/s, % of MI355X roofline, Kimi-shape N=64 tree",
@@ -224,7 +241,14 @@ def run(args):
         "alg_mbytes_per_step": round(nbytes / 1e6, 4),
         "attn_kernel_ms": round(attn_ms, 5),
         "attn_kernel_ms_p10_p50_p90": [round(float(np.percentile(attn_each, q)), 5) for q in (10, 50, 90)],
-        "attn_kernel_cold_ms_median": round(float(np.median(cold)), 5) if cold else None,
+        "attn_kernel_cold_ms_median": round(cold_ms, 5) if cold else None,
+        "step_cold_ms_median": round(cold_step_ms, 5) if cold_step else None,
+        # the binding roof's fraction over other regions: the attention launch with cold caches,
+        # and the whole step (prepare + attention + combine), hot and cold
+        "frac_attn_cold": frac(cold_ms),
+        "frac_step_hot": frac(step_ms),
+        "frac_step_cold": frac(cold_step_ms),
+        "output_check": check,
         "arith_intensity_flop_per_byte": round(flops / nbytes, 1),
         "kernel_source_hash": kernel_source_hash(),
         "wall_ms_timed_region": round(wall_ms, 3),
@@ -239,6 +263,49 @@ def run(args):
         },
     }
     return line, inp
+
+
+def check_outputs(inp, masks, out):
+    """Compare the device masks and outputs of a finished step with the fp64 oracle; exits
+    with an error when they differ.  Returns a short description of what was compared."""
+    import oracle
+    sp = inp.spec
+    ref_masks, _ = oracle.visibility(inp.parents.numpy())
+    if not np.array_equal(masks.cpu().numpy().view(np.uint64), ref_masks):
+        raise SystemExit("masks differ from the oracle on the benchmark inputs")
+    flops, _, _ = algorithmic_work(inp)
+    R = sp.nodes * sp.heads
+    total = sp.batch * R
+    if flops <= 40e9:
+        rows = None
+    else:
+        rng = np.random.default_rng(12345)
+        per_group = [b * R + np.minimum(np.arange(0, R, 32) + rng.integers(0, 32, size=(R + 31) // 32), R - 1)
+                     for b in range(sp.batch)]
+        rows = np.unique(np.concatenate(per_group + [rng.integers(0, total, size=256)]))
+    cores = len(os.sched_getaffinity(0))
+    ref = oracle.run(inp, rows=rows, threads=cores)[1].reshape(-1, sp.d_latent)
+    got = out.reshape(-1, sp.d_latent)
+    if rows is not None:
+        got = got[torch.from_numpy(rows).to(out.device)]
+    got = got.cpu().double().numpy()
+    err = float(np.abs(got - ref).max())
+    tol = 2e-3 if sp.dtype == "bf16" else 1e-5
+    if not np.isfinite(got).all() or err > tol:
+        raise SystemExit(f"attention max-abs error {err} above {tol} on the benchmark inputs")
+    what = f"all {total} rows" if rows is None else f"{rows.size} of {total} rows (one per 32-row group + random)"
+    return {"masks": "bit-exact", "rows": what, "max_abs_err": float(f"{err:.3e}"), "tol": tol}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0):
@@ -258,7 +325,7 @@ def cpu_baseline(inp, min_seconds=10.0, max_seconds=30.0):
     rows = inp.spec.batch * inp.spec.nodes * inp.spec.heads
     return {"value": round(reps * flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} whole step(s) of the same workload (masks + all {rows} rows, fp64) "
-                      f"in {dt:.2f} s on {cores} threads"}
+                      f"in {dt:.2f} s on {cores} threads", "cpu_model": cpu_model()}
 
 
 def accept_inputs(inp, seed):
@@ -646,32 +713,38 @@ def run_step_row(args):
 
 
 # HBM traffic of the attention kernel per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-# summarised under profiles/.  The summary records a hash of the kernel sources it was taken
-# on; when the sources have changed since, the figure no longer describes this kernel and
-# `traffic` is reported as null.
-# Sources each kernel is compiled from (a change to any other file leaves it as it was).
+# summarised under profiles/.  The summary records a hash of the code the kernel is built from;
+# when that code has changed since, the figure no longer describes this kernel and `traffic` is
+# reported as null.  The hash covers each kernel's own sources, the C-ABI layer that sets its
+# launch geometry (split policy, tile sizes, workspace layout) and the public header, and the
+# compiler flags of the build.
+_ABI = ["tree_verify_mla_02_amd/csrc/api.cpp", "include/kdt.h", "tree_verify_mla_02_amd/csrc/kdt_internal.h"]
 KERNEL_SOURCES = {
-    "verify_attn": ["verify_attn.hip", "kdt_internal.h"],
-    "kv_compact": ["accept.hip", "kdt_internal.h"],
-    "tree_accept": ["accept.hip", "kdt_internal.h"],
-    "tree_build": ["tree_build.hip", "kdt_internal.h"],
+    "verify_attn": ["tree_verify_mla_02_amd/csrc/verify_attn.hip",
+                    "tree_verify_mla_02_amd/csrc/visibility_rows.h"] + _ABI,
+    "kv_compact": ["tree_verify_mla_02_amd/csrc/accept.hip"] + _ABI,
+    "tree_accept": ["tree_verify_mla_02_amd/csrc/accept.hip"] + _ABI,
+    "tree_build": ["tree_verify_mla_02_amd/csrc/tree_build.hip"] + _ABI,
 }
 
 
 def kernel_source_hash(kernel: str = "verify_attn") -> str:
-    """Hash of the code a kernel is compiled from: its sources with comments, blank lines and
-    trailing blanks removed, so that an edit of a comment leaves it unchanged."""
+    """Hash of the code a kernel is compiled from (its sources with comments, blank lines and
+    trailing blanks removed, so that an edit of a comment leaves it unchanged) and of the build
+    flags."""
     import hashlib
     import re
+
+    from tree_verify_mla_02_amd import build as kbuild
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "tree_verify_mla_02_amd", "csrc")
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, name)) as fh:
+        with open(os.path.join(ROOT, name)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
         code = "\n".join(ln for ln in lines if ln.strip())
         h.update(name.encode() + b"\0" + code.encode())
+    h.update(b"flags\0" + " ".join(kbuild.FLAGS).encode())
     return h.hexdigest()[:16]
 
 

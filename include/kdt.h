@@ -4,9 +4,9 @@
  * The operation.  A speculative decoder drafts candidate tokens as a tree and the
  * target model verifies every node of that tree in one batched forward pass ("The
  * Capstone Validation: Writing the DDTree Speculative Decode Test", section "Context and
- * Motivation").  Inside that pass, attention is "tree-verify MLA-absorb attention with
- * visibility masking" ("Validating the Native Engine: The Autoregressive Test Driver for
- * Kimi K2.6 DDTree Inference", section "The Broader Context"): with Multi-head Latent
+ * Motivation").  Inside that pass the engine runs a tree-verify attention kernel for
+ * absorbed MLA, masked by tree visibility ("Validating the Native Engine: The Autoregressive
+ * Test Driver for Kimi K2.6 DDTree Inference", section "The Broader Context"): with Multi-head Latent
  * Attention in absorbed form, all heads share one latent KV row per token (a d_latent
  * wide latent plus a d_rope wide rotary key), and every tree node must attend to exactly
  * what an ordinary decode of its own root-to-node path would attend to -- the committed
@@ -107,11 +107,19 @@ int kdt_build_visibility(const int32_t *parents, int32_t batch, int32_t num_node
 
 /* Bytes of device workspace kdt_tree_verify_* need for `desc` on the current device
  * (plan, per-request offsets, and split-KV partials when the batch is too small to fill
- * the GPU).  Returns 0 when desc is invalid (see kdt_last_error()). */
+ * the GPU).  Returns 0 when desc is invalid (see kdt_last_error()).  The pages fix no
+ * workspace; it exists because the verify pass of "The Capstone Validation" (section
+ * "Broader Significance": verify passes are attention-bound and scale with context length)
+ * must spread long caches over the whole GPU. */
 size_t kdt_tree_verify_workspace_size(const kdt_verify_desc *desc);
 
 /*
- * kdt_tree_verify_attn -- the whole verify attention: plan + attend + combine.
+ * kdt_tree_verify_attn -- the whole verify attention: plan + attend + combine.  This is the
+ * engine's visibility-masked tree-verify attention for absorbed MLA ("Validating the Native
+ * Engine", section "The Broader Context"), applied to the tree of candidates that "The Capstone
+ * Validation", section "Context and Motivation", verifies in one batched pass: each node's
+ * output is the attention a plain decode of its own root-to-node path would compute (the
+ * formula at the top of this file).
  *   q_lat      [B, N, H, d_c] rows at q_lat_stride;  q_rope [B, N, H, d_r] at q_rope_stride.
  *   ckv_cache  [T, d_c], krope_cache [T, d_r]: committed caches of all requests packed in
  *              request order (request b owns rows off_b .. off_b + cache_lens[b] - 1 with
@@ -133,7 +141,9 @@ int kdt_tree_verify_attn(const void *q_lat, const void *q_rope, const void *ckv_
 
 /*
  * The same operation in three stream-ordered stages, for callers that reuse one plan for
- * every layer of a verify pass (the cache lengths do not change between layers).
+ * every layer of a verify pass (the cache lengths do not change between layers: the verify
+ * pass of "The Capstone Validation", section "Context and Motivation", runs every layer of the
+ * target over the same drafted tree and the same committed cache).
  *   kdt_tree_verify_plan    validates cache_lens, builds per-request offsets and the
  *                           longest-first work list in `workspace`.
  *   kdt_tree_verify_attend  the attention kernel; needs a plan for the same desc in
@@ -154,7 +164,9 @@ int kdt_tree_verify_combine(float *out, const kdt_verify_desc *desc, void *works
 
 /*
  * kdt_tree_verify_prepare -- kdt_build_visibility and kdt_tree_verify_plan in one launch
- * (the two are independent; a verify step needs both before the attention).
+ * (the two are independent; a verify step needs both before the attention: the visibility
+ * masks of "Validating the Native Engine", section "The Broader Context", and the ragged work
+ * list of the batch).
  *   parents   [B, N] int32, device, with B = desc->batch and N = desc->num_nodes; bitmask
  *             [B, N, ceil(N/64)] uint64 -- exactly as kdt_build_visibility.
  *   cache_lens, workspace, dev_status -- exactly as kdt_tree_verify_plan.

@@ -1,5 +1,5 @@
 """Shared helpers of the GPU tests: move a workloads.Inputs batch to the device and run the
-C-ABI path on it; pick sampled rows for oracle checks at full size."""
+C-ABI path on it."""
 from __future__ import annotations
 
 import dataclasses
@@ -84,20 +84,6 @@ def run_gpu(inp: workloads.Inputs, dev: DevInputs = None, staged=False):
         kdt.combine(out, desc, ws)
     torch.cuda.synchronize()
     return masks.cpu().numpy().view(np.uint64), out, int(status.item())
-
-
-def sample_rows(inp: workloads.Inputs, per_request: int = 12, seed: int = 0):
-    """Flat row ids: first/last row of every request, rows around 128-row tile edges, random rows."""
-    sp = inp.spec
-    R = sp.nodes * sp.heads
-    rng = np.random.default_rng(seed)
-    rows = set()
-    for b in range(sp.batch):
-        base = b * R
-        cand = [0, R - 1, min(127, R - 1), min(128, R - 1), R // 2]
-        cand += list(rng.integers(0, R, size=per_request))
-        rows.update(base + int(c) for c in cand)
-    return np.array(sorted(rows), dtype=np.int64)
 
 
 def report(name: str, err: float, tol: float):

@@ -9,9 +9,16 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 
+def _fake_tree(tmp_path):
+    for name in bench.KERNEL_SOURCES["verify_attn"]:
+        path = tmp_path / name
+        path.parent.mkdir(parents=True, exist_ok=True)
+        path.write_text("int unchanged;\n")
+    return tmp_path / "tree_verify_mla_02_amd" / "csrc"
+
+
 def test_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
-    csrc = tmp_path / "tree_verify_mla_02_amd" / "csrc"
-    csrc.mkdir(parents=True)
+    csrc = _fake_tree(tmp_path)
     (csrc / "verify_attn.hip").write_text("int f(int x) {\n  return x + 1;  // one\n}\n")
     (csrc / "kdt_internal.h").write_text("/* header */\n#pragma once\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
@@ -24,11 +31,24 @@ def test_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.kernel_source_hash("verify_attn") != h0
 
 
+def test_hash_covers_launch_geometry_and_flags(tmp_path, monkeypatch):
+    """The split policy lives in the C-ABI layer: a change there (or to the build flags) must
+    void a recorded traffic figure too."""
+    csrc = _fake_tree(tmp_path)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash("verify_attn")
+    (csrc / "api.cpp").write_text("int chunk = 512;\n")
+    h1 = bench.kernel_source_hash("verify_attn")
+    assert h1 != h0
+    from tree_verify_mla_02_amd import build as kbuild
+    monkeypatch.setattr(kbuild, "FLAGS", kbuild.FLAGS + ["-DKDT_MIN_CHUNK=128"])
+    assert bench.kernel_source_hash("verify_attn") != h1
+
+
 def test_every_kernel_source_exists():
-    csrc = os.path.join(ROOT, "tree_verify_mla_02_amd", "csrc")
     for kernel, names in bench.KERNEL_SOURCES.items():
         for n in names:
-            assert os.path.exists(os.path.join(csrc, n)), (kernel, n)
+            assert os.path.exists(os.path.join(ROOT, n)), (kernel, n)
         assert len(bench.kernel_source_hash(kernel)) == 16
 
 

@@ -175,15 +175,13 @@ def build_visibility(parents: torch.Tensor, out: Optional[torch.Tensor] = None,
     return out
 
 
-def tree_verify_attn(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, bitmask, cache_lens, scale: float,
-                     out=None, workspace=None, dev_status=None, max_cache_len: Optional[int] = None,
+def tree_verify_attn(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, bitmask, cache_lens, scale: float, *,
+                     max_cache_len: int, out=None, workspace=None, dev_status=None,
                      total_cache_len: Optional[int] = None, stream=None) -> torch.Tensor:
     """Tree-verify MLA-absorb attention; returns out [B, N, H, d_c] fp32.
 
-    max_cache_len is a host-side bound on cache_lens; when omitted it is read back from the
-    device (one synchronisation)."""
-    if max_cache_len is None:
-        max_cache_len = int(cache_lens.max().item()) if cache_lens.numel() else 0
+    max_cache_len is a host-side upper bound on cache_lens (required: reading it back from the
+    device would synchronise the host)."""
     desc = make_desc(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, max_cache_len, total_cache_len)
     B, N, H, dc = q_lat.shape
     if out is None:
@@ -287,3 +285,4 @@ def kv_compact(ckv, krope, cache_lens, tree_ckv, tree_krope, path, accept_len, d
                                  _ptr(path), _ptr(accept_len), _ptr(ckv_out), _ptr(krope_out), _ptr(new_lens),
                                  int(capacity_rows), ctypes.byref(desc), _ptr(dev_status), _stream(stream)))
     return new_lens
+

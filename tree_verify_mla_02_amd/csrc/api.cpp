@@ -148,6 +148,8 @@ kdt::AttnArgs make_args(const kdt_verify_desc &d, const kdt::Geometry &g, void *
 
 namespace kdt {
 
+int set_error(int code, const char *msg) { return fail(code, "%s", msg); }
+
 bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     Geometry x{};
     x.rows = (int64_t)d.num_nodes * d.num_heads;
@@ -205,12 +207,11 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     x.off_header = take(sizeof(WsHeader));
     x.off_offsets = take(8 * B);
     x.off_lens = take(4 * B);
-    x.off_gwork = take(8 * (size_t)groups);
-    x.off_gorder = take(4 * (size_t)groups);
     x.off_units = take(sizeof(kdt::Unit) * (size_t)x.units);
     if (S > 1) {
         x.off_ml = take(8 * (size_t)B * S * x.rows);
-        x.off_o = take(3 * (size_t)B * S * rt128 * kRowsPerTile * d.d_latent);   // whole 128-row tiles, 24-bit
+        // whole 128-row tiles; 3 words per 4 values (24-bit) for bf16, 4 for fp32
+        x.off_o = take((size_t)partial_words(d.dtype) * B * S * rt128 * kRowsPerTile * d.d_latent);
     } else {
         x.off_ml = x.off_o = 0;
     }
@@ -416,7 +417,7 @@ int kdt_tree_verify_combine(float *out, const kdt_verify_desc *desc, void *works
     if (g.nsplit <= 1) return ok();
     kdt::AttnArgs a = make_args(*desc, g, workspace);
     a.out = out;
-    const hipError_t e = kdt::launch_combine(a, desc->d_latent, (hipStream_t)stream);
+    const hipError_t e = kdt::launch_combine(a, desc->d_latent, desc->dtype, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     return ok();
 }

@@ -38,8 +38,12 @@ struct Geometry {
     int64_t groups;        // G = B * ceil(RT / bt) * ceil(S / bs)
     int mask_words;        // W = ceil(N / 64)
     // workspace layout (byte offsets, 256-aligned)
-    size_t off_header, off_offsets, off_lens, off_gwork, off_gorder, off_units, off_ml, off_o, total_bytes;
+    size_t off_header, off_offsets, off_lens, off_units, off_ml, off_o, total_bytes;
 };
+
+// Records `code` and `msg` as the calling thread's last status and error (kdt_last_status,
+// kdt_last_error) and returns code.
+int set_error(int code, const char *msg);
 
 // Fills g from desc for a device with `num_cus` compute units.  Returns false on overflow.
 bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g);
@@ -76,8 +80,9 @@ struct AttnArgs {
     const int32_t *lens;
     const Unit *units;     // one per grid slot
     float2 *part_ml;       // [B][S][R] (running max in log2 domain, sum)
-    uint32_t *part_o;      // un-normalised partial outputs as packed 24-bit floats, per wave
-                           // in register order: block ((b*S + s)*RT + rt)*4 + wave of 32 rows x d_c
+    uint32_t *part_o;      // un-normalised partial outputs, per wave in register order: block
+                           // ((b*S + s)*RT + rt)*4 + wave of 32 rows x d_c values, as packed
+                           // 24-bit floats (bf16 inputs) or plain fp32 (fp32 inputs)
 };
 
 hipError_t launch_visibility(const int32_t *parents, int B, int N, uint64_t *masks,
@@ -89,7 +94,11 @@ hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t
                           hipStream_t st);
 hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units,
                          hipStream_t st);
-hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st);
+hipError_t launch_combine(const AttnArgs &a, int d_latent, int dtype, hipStream_t st);
+
+// 32-bit words of split-partial storage per 4 output values: 3 (24-bit floats) for bf16
+// inputs, 4 (fp32) for fp32 inputs.
+constexpr int partial_words(int dtype) { return dtype == KDT_F32 ? 4 : 3; }
 hipError_t launch_accept(const int32_t *parents, const int32_t *tokens, const int32_t *target_next,
                          const int32_t *root_next, int B, int N, int32_t *path, int32_t *accept_len,
                          int32_t *bonus, hipStream_t st);

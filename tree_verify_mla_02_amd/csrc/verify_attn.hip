@@ -102,16 +102,15 @@ struct PlanArgs {
     WsHeader *hdr;
     int64_t *offsets;
     int32_t *lens;
-    int64_t *gwork;
-    int32_t *gorder;
     Unit *units;
     int32_t *dev_status;
     FastDiv fd_chunk, fd_per, fd_grgs, fd_gs, fd_gr, fd_bs;
 };
 
-// LDS of the plan: the lengths and offsets of up to kMaxLdsReq requests, and the group work
-// and order of up to kMaxSortGroups groups, so that every step after the first load of
-// cache_lens reads LDS (larger batches fall back to the workspace copies).
+// LDS of the plan: the lengths and offsets of up to kMaxLdsReq requests, and the sort keys and
+// work order of up to kMaxSortGroups groups, so that every step after the first load of
+// cache_lens reads LDS (more requests read the workspace copies of lengths and offsets; more
+// groups keep request order).
 constexpr int kMaxLdsReq = 1024;
 struct alignas(16) PlanLds {
     uint32_t key[kMaxSortGroups];       // sort key of each group (see plan_body); 16-byte reads
@@ -217,33 +216,26 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, PlanLds &L) {
     const int G = B * GR * GS;
     const int per = bt * bs;
     const bool grp_lds = G <= kMaxSortGroups;
-    uint32_t *key = L.key;
-    int32_t *order = grp_lds ? L.order : pa.gorder;
-    for (int g = tid; g < G; g += nth) {
-        const uint32_t q = fdiv((uint32_t)g, pa.fd_gs);
-        const int b = (int)fdiv((uint32_t)g, pa.fd_grgs), gs = g - (int)q * GS;
-        const int len = lens[b];
-        int64_t w = -1;
-        if (ok) {
-            const int sbr = req_lds ? L.sb[b] : splits(len);
-            for (int sp = gs * bs; sp < gs * bs + bs && sp < sbr; sp++) {
-                const int64_t left = (int64_t)len - (int64_t)sp * chunk;
-                w = (w < 0 ? 0 : w) + (left < chunk ? (left > 0 ? left : 0) : chunk) + (sp == 0 ? N : 0);
+    if (grp_lds) {
+        uint32_t *key = L.key;
+        for (int g = tid; g < G; g += nth) {
+            const uint32_t q = fdiv((uint32_t)g, pa.fd_gs);
+            const int b = (int)fdiv((uint32_t)g, pa.fd_grgs), gs = g - (int)q * GS;
+            const int len = lens[b];
+            int64_t w = -1;
+            if (ok) {
+                const int sbr = req_lds ? L.sb[b] : splits(len);
+                for (int sp = gs * bs; sp < gs * bs + bs && sp < sbr; sp++) {
+                    const int64_t left = (int64_t)len - (int64_t)sp * chunk;
+                    w = (w < 0 ? 0 : w) + (left < chunk ? (left > 0 ? left : 0) : chunk) + (sp == 0 ? N : 0);
+                }
             }
-        }
-        if (grp_lds) {
             const int64_t tiles = w < 0 ? 0 : (w + kKeysPerTile - 1) / kKeysPerTile;
             key[g] = (w < 0 ? 0u : 0x80000000u) | ((uint32_t)(tiles < 0xfffff ? tiles : 0xfffff) << 11) |
                      (uint32_t)(2047 - g);
-        } else {
-            pa.gwork[g] = w;
         }
-    }
-    if (grp_lds)                         // pad to whole 4-key reads: key 0 ranks below any group
-        for (int g = G + tid; g < ((G + 3) & ~3); g += nth) key[g] = 0u;
-    for (int u = tid; u < U; u += nth) pa.units[u] = Unit{-1, 0, 0, 0, 0, 0, 0};
-    if (grp_lds) lds_sync(); else __syncthreads();
-    if (grp_lds) {
+        for (int g = G + tid; g < ((G + 3) & ~3); g += nth) key[g] = 0u;   // whole 4-key reads: 0 ranks last
+        lds_sync();
         // rank = #{h : key[h] > key[g]}: every thread reads the same keys (LDS broadcasts), four
         // per read, eight reads in flight
         const int G4 = (G + 3) >> 2;
@@ -263,35 +255,40 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, PlanLds &L) {
                 const uint4 v = key4[h];
                 rank += (v.x > kg) + (v.y > kg) + (v.z > kg) + (v.w > kg);
             }
-            order[rank] = g;
+            L.order[rank] = g;
         }
         lds_sync();
-    } else {
-        for (int g = tid; g < G; g += nth) order[g] = g;
-        __syncthreads();
     }
-    // Group p (in work order) goes to XCD lane x in snake order over rounds of 8 groups; its
-    // unit i takes grid slot x + 8 * (round * per + i).  Slots are dealt to the XCDs
-    // round-robin, so a group runs on one XCD.
-    for (int e = tid; e < G * per; e += nth) {
-        const int p = (int)fdiv((uint32_t)e, pa.fd_per);
-        const int i = e - p * per;
-        const int g = order[p];
-        if (grp_lds ? !(key[g] >> 31) : pa.gwork[g] < 0) continue;
-        const uint32_t q = fdiv((uint32_t)g, pa.fd_gs);
-        const int b = (int)fdiv((uint32_t)g, pa.fd_grgs);
-        const int gs = g - (int)q * GS, gr = (int)q - (int)fdiv(q, pa.fd_gr) * GR;
-        const int ib = (int)fdiv((uint32_t)i, pa.fd_bs);
-        const int rt = gr * bt + ib, sp = gs * bs + (i - ib * bs);
-        const int len = lens[b];
-        const int sb = req_lds ? L.sb[b] : splits(len);
-        if (rt >= RT || sp >= sb) continue;
-        const int round = p >> 3;        // kXcds = 8
-        const int j = p & 7;
-        const int x = (round & 1) ? kXcds - 1 - j : j;
-        const int64_t k0 = (int64_t)sp * chunk;
-        const int64_t k1 = k0 + chunk < (int64_t)len ? k0 + chunk : (int64_t)len;
-        pa.units[x + kXcds * (round * per + i)] = Unit{b, rt, sp, sb, (int32_t)k0, (int32_t)k1, offs[b] + k0};
+    // Group p (in work order; request order above kMaxSortGroups groups) goes to XCD lane x in
+    // snake order over rounds of 8 groups, and its unit i takes grid slot x + 8 * (round * per + i).
+    // Slots are dealt to the XCDs round-robin, so a group runs on one XCD.  The loop runs over the
+    // slots and inverts that map, so that every slot is stored exactly once: a slot no unit takes
+    // (padding, a split past the request's keys, a row tile past its rows, rejected lengths) gets
+    // the empty record.  A group with no work has no split below its request's split count, so
+    // the per-slot test covers it.
+    for (int u = tid; u < U; u += nth) {
+        const int x = u & (kXcds - 1);
+        const int k = u >> 3;                 // kXcds = 8
+        const int round = (int)fdiv((uint32_t)k, pa.fd_per);
+        const int i = k - round * per;
+        const int p = round * kXcds + ((round & 1) ? kXcds - 1 - x : x);
+        Unit un{-1, 0, 0, 0, 0, 0, 0};
+        if (ok && p < G) {
+            const int g = grp_lds ? L.order[p] : p;
+            const uint32_t q = fdiv((uint32_t)g, pa.fd_gs);
+            const int b = (int)fdiv((uint32_t)g, pa.fd_grgs);
+            const int gs = g - (int)q * GS, gr = (int)q - (int)fdiv(q, pa.fd_gr) * GR;
+            const int ib = (int)fdiv((uint32_t)i, pa.fd_bs);
+            const int rt = gr * bt + ib, sp = gs * bs + (i - ib * bs);
+            const int len = lens[b];
+            const int sb = req_lds ? L.sb[b] : splits(len);
+            if (rt < RT && sp < sb) {
+                const int64_t k0 = (int64_t)sp * chunk;
+                const int64_t k1 = k0 + chunk < (int64_t)len ? k0 + chunk : (int64_t)len;
+                un = Unit{b, rt, sp, sb, (int32_t)k0, (int32_t)k1, offs[b] + k0};
+            }
+        }
+        pa.units[u] = un;
     }
 }
 
@@ -791,10 +788,12 @@ __device__ __forceinline__ void pv_pair(const LDS_AS char *buf, const u32x4 (&ph
     });
 }
 
-// Split partials are stored as 24-bit floats: the top 24 bits of the fp32 value (sign,
-// exponent, 15 mantissa bits) rounded to nearest even -- relative error <= 2^-17, far inside
-// the output tolerance -- 4 values in 3 words.  The partial round trip through memory (the
-// cost of splitting keys over workgroups) is a quarter smaller.
+// Split partials of bf16 requests are stored as 24-bit floats: the top 24 bits of the fp32
+// value (sign, exponent, 15 mantissa bits) rounded to nearest even -- relative error <= 2^-16,
+// far inside the 2e-3 output tolerance -- 4 values in 3 words, so the partial round trip
+// through memory (the cost of splitting keys over workgroups) is a quarter smaller.  fp32
+// requests keep plain fp32 partials: 2^-16 of an output of magnitude 1 is already above their
+// 1e-5 tolerance.
 __device__ __forceinline__ uint32_t to24(float x) {
     const uint32_t u = __float_as_uint(x);
     return (u + 0x7fu + ((u >> 8) & 1u)) >> 8;
@@ -810,6 +809,24 @@ __device__ __forceinline__ float4 unpack24x4(const uint32_t *src) {
     const uint32_t p = src[0], q = src[1], r = src[2];
     return make_float4(from24(p & 0xffffffu), from24((p >> 24) | ((q & 0xffffu) << 8)),
                        from24((q >> 16) | ((r & 0xffu) << 16)), from24(r >> 8));
+}
+
+// Store / load of 4 partial values in the format of the input type: kPartWords<T> words each.
+template <typename T>
+constexpr int kPartWords = std::is_same<T, float>::value ? 4 : 3;
+template <typename T>
+__device__ __forceinline__ void store_part4(uint32_t *dst, float a, float b, float c, float d) {
+    if constexpr (kPartWords<T> == 4)
+        *(float4 *)dst = make_float4(a, b, c, d);
+    else
+        pack24x4(dst, a, b, c, d);
+}
+template <bool F32>
+__device__ __forceinline__ float4 load_part4(const uint32_t *src) {
+    if constexpr (F32)
+        return *(const float4 *)src;
+    else
+        return unpack24x4(src);
 }
 
 template <typename T, int DC, int DR>
@@ -1088,18 +1105,19 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             }
     } else {
         // Partials keep the wave's register order: block ((b*S + s)*RT + rt)*4 + wave holds the
-        // wave's 32 rows, and the 4 values (t16, g) of lane l, packed to 3 words, sit at words
-        // ((t16*4 + g)*64 + l)*3, so every store instruction writes 768 contiguous bytes (the
-        // row-major order would write 32 rows x 32 bytes).  The combine reads the same order.
+        // wave's 32 rows, and the 4 values (t16, g) of lane l, in PW words, sit at words
+        // ((t16*4 + g)*64 + l)*PW, so every store instruction writes 64*PW*4 contiguous bytes
+        // (the row-major order would write 32 rows x 32 bytes).  The combine reads the same order.
+        constexpr int PW = kPartWords<T>;
         const int64_t prow = ((int64_t)b * a.S + s) * R + r;
         const int64_t blk = (((int64_t)b * a.S + s) * a.RT + rt) * kWaves + wave;
-        uint32_t *dst = a.part_o + blk * (kRowsPerWave * DC / 4 * 3) + lane * 3;
+        uint32_t *dst = a.part_o + blk * (kRowsPerWave * DC / 4 * PW) + lane * PW;
 #pragma unroll
         for (int t16 = 0; t16 < NT16; t16++)
 #pragma unroll
             for (int g = 0; g < 4; g++)
-                pack24x4(dst + (t16 * 4 + g) * 192, o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2],
-                         o[t16][4 * g + 3]);
+                store_part4<T>(dst + (t16 * 4 + g) * 64 * PW, o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2],
+                               o[t16][4 * g + 3]);
         if (half == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
     }
 }
@@ -1389,13 +1407,14 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
         const int64_t prow = ((int64_t)b * a.S + s) * R + r;
         // 32-row group 2*rt64 + rh of the request = group (rt64 & 1)*2 + rh of 128-row tile rt64/2
         const int64_t blk = (((int64_t)b * a.S + s) * a.RT + (rt64 >> 1)) * kWaves + (rt64 & 1) * 2 + rh;
-        uint32_t *dst = a.part_o + blk * (kRowsPerWave * DC / 4 * 3) + lane * 3;
+        constexpr int PW = kPartWords<T>;
+        uint32_t *dst = a.part_o + blk * (kRowsPerWave * DC / 4 * PW) + lane * PW;
 #pragma unroll
         for (int t16 = 0; t16 < NT16; t16++)
 #pragma unroll
             for (int g = 0; g < 4; g++)
-                pack24x4(dst + (t16 * 4 + g) * 192, o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2],
-                         o[t16][4 * g + 3]);
+                store_part4<T>(dst + (t16 * 4 + g) * 64 * PW, o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2],
+                               o[t16][4 * g + 3]);
         if (half == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
     }
 }
@@ -1408,9 +1427,10 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
 // flight.  With WS = 1 each wave of a workgroup takes its own tile; with WS = 2 or 4 (more
 // splits) WS waves share one tile, wave w of them taking splits w, w+WS, ..., and their
 // results are merged in LDS: more waves, fewer loads each, for the same bytes.
-template <int DC, int WS, int GC>
+template <int DC, int WS, int GC, bool F32P>
 __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kernel(AttnArgs a) {
     constexpr int NT16 = DC / 32;
+    constexpr int PW = F32P ? 4 : 3;                  // partial words per 4 values
     constexpr int NSUB = 4 / GC;                      // waves over one tile's 4 column groups
     constexpr int NW = WS > kWaves ? WS : kWaves;     // waves per workgroup
     static_assert(NW % WS == 0 && (NT16 * NSUB) % (NW / WS) == 0 || WS == 1, "tiles of a workgroup share a row group");
@@ -1450,9 +1470,9 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
             if (sp < sb) {
                 ml[u] = a.part_ml[((int64_t)b * a.S + sp) * a.R + rc];
                 const int64_t blk = (((int64_t)b * a.S + sp) * a.RT + rt) * kWaves + wave;
-                const uint32_t *src = a.part_o + blk * (kRowsPerWave * DC / 4 * 3) + lane * 3;
+                const uint32_t *src = a.part_o + blk * (kRowsPerWave * DC / 4 * PW) + lane * PW;
 #pragma unroll
-                for (int g = 0; g < GC; g++) x[u][g] = unpack24x4(src + (t16 * 4 + sub * GC + g) * 192);
+                for (int g = 0; g < GC; g++) x[u][g] = load_part4<F32P>(src + (t16 * 4 + sub * GC + g) * 64 * PW);
             }
         }
 #pragma unroll
@@ -1530,8 +1550,6 @@ static PlanArgs plan_args(const int32_t *cache_lens, const kdt_verify_desc &d, c
     pa.hdr = (WsHeader *)(w + g.off_header);
     pa.offsets = (int64_t *)(w + g.off_offsets);
     pa.lens = (int32_t *)(w + g.off_lens);
-    pa.gwork = (int64_t *)(w + g.off_gwork);
-    pa.gorder = (int32_t *)(w + g.off_gorder);
     pa.units = (Unit *)(w + g.off_units);
     pa.dev_status = dev_status;
     const int GR = (g.row_tiles + g.bt - 1) / g.bt, GS = (g.nsplit + g.bs - 1) / g.bs;
@@ -1585,7 +1603,7 @@ hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype,
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st) {
+hipError_t launch_combine(const AttnArgs &a, int d_latent, int dtype, hipStream_t st) {
     const int64_t tiles = (int64_t)a.B * ((a.R + kRowsPerWave - 1) / kRowsPerWave) * (d_latent / 32);
     // Waves per tile: first more waves share a tile (each keeping at least 4 splits), then a
     // tile's four column groups go to 2 or 4 waves, while the grid stays within about 8 waves
@@ -1600,25 +1618,28 @@ hipError_t launch_combine(const AttnArgs &a, int d_latent, hipStream_t st) {
     const int64_t tpb = nw / ws;
     const unsigned grid = (unsigned)((subs + tpb - 1) / tpb);
     const unsigned block = (unsigned)(64 * nw);
-    auto go = [&](auto dc, auto gcv) {
+    auto go = [&](auto dc, auto gcv, auto f32p) {
         constexpr int DCv = decltype(dc)::value, GC = decltype(gcv)::value;
+        constexpr bool F = decltype(f32p)::value;
         switch (ws) {
-            case 16: combine_kernel<DCv, 16, GC><<<grid, block, 0, st>>>(a); break;
-            case 8: combine_kernel<DCv, 8, GC><<<grid, block, 0, st>>>(a); break;
-            case 4: combine_kernel<DCv, 4, GC><<<grid, block, 0, st>>>(a); break;
-            case 2: combine_kernel<DCv, 2, GC><<<grid, block, 0, st>>>(a); break;
-            default: combine_kernel<DCv, 1, GC><<<grid, block, 0, st>>>(a); break;
+            case 16: combine_kernel<DCv, 16, GC, F><<<grid, block, 0, st>>>(a); break;
+            case 8: combine_kernel<DCv, 8, GC, F><<<grid, block, 0, st>>>(a); break;
+            case 4: combine_kernel<DCv, 4, GC, F><<<grid, block, 0, st>>>(a); break;
+            case 2: combine_kernel<DCv, 2, GC, F><<<grid, block, 0, st>>>(a); break;
+            default: combine_kernel<DCv, 1, GC, F><<<grid, block, 0, st>>>(a); break;
         }
     };
-    auto go_dc = [&](auto dc) {
-        if (gc == 4) go(dc, std::integral_constant<int, 4>{});
-        else if (gc == 2) go(dc, std::integral_constant<int, 2>{});
-        else go(dc, std::integral_constant<int, 1>{});
+    auto go_dc = [&](auto dc, auto f32p) {
+        if (gc == 4) go(dc, std::integral_constant<int, 4>{}, f32p);
+        else if (gc == 2) go(dc, std::integral_constant<int, 2>{}, f32p);
+        else go(dc, std::integral_constant<int, 1>{}, f32p);
     };
-    if (d_latent == 512) {
-        go_dc(std::integral_constant<int, 512>{});
-    } else if (d_latent == 64) {
-        go_dc(std::integral_constant<int, 64>{});
+    if (d_latent == 512 && dtype == KDT_BF16) {
+        go_dc(std::integral_constant<int, 512>{}, std::false_type{});
+    } else if (d_latent == 64 && dtype == KDT_BF16) {
+        go_dc(std::integral_constant<int, 64>{}, std::false_type{});
+    } else if (d_latent == 64 && dtype == KDT_F32) {
+        go_dc(std::integral_constant<int, 64>{}, std::true_type{});
     } else {
         return hipErrorInvalidValue;
     }

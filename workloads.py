@@ -72,6 +72,10 @@ SPECS: Dict[str, Spec] = {
     # (budget 7 = block size 8 minus the bonus token)
     "decode": Spec("decode", 6, 1, 1, 64, 512, 64, "bf16", 32768, tree="chain"),
     "block8": Spec("block8", 7, 1, 7, 64, 512, 64, "bf16", 4096, depth=7, topk=8),
+    # prefill-shaped chains: a causal chunk of 256 tokens (the most nodes one call takes) over a
+    # 4096- and a 32768-token committed cache
+    "prefill4k": Spec("prefill4k", 8, 1, 256, 64, 512, 64, "bf16", 4096, tree="chain"),
+    "prefill": Spec("prefill", 9, 1, 256, 64, 512, 64, "bf16", 32768, tree="chain"),
 }
 
 
