@@ -1,5 +1,5 @@
 """Host-side checks of the C ABI that need no GPU: the library loads, exports every
-function include/kdt.h declares, and rejects bad arguments before touching the device."""
+function include/*.h declares, and rejects bad arguments before touching the device."""
 import ctypes
 import os
 import re
@@ -13,9 +13,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def declared_functions():
-    src = open(os.path.join(ROOT, "include", "kdt.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kdt_[a-z_]+)\s*\(", src)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            src = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, h)).read(), flags=re.S)
+            names.update(re.findall(r"\b(kdt_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -144,3 +148,14 @@ def test_build_tree_rejects_bad_arguments_on_host():
     assert call(N=0) == _lib.KDT_ERR_UNSUPPORTED
     assert call(N=257) == _lib.KDT_ERR_UNSUPPORTED
     assert call(tok=ctypes.c_void_p((1 << 20) + 2)) == _lib.KDT_ERR_MISALIGNED
+
+
+def test_noalloc_rejects_bad_desc_on_host():
+    """The allocation-free entry point validates the batch before it looks at its scratch array."""
+    lib = kdt.load()
+    fake = ctypes.c_void_p(1 << 20)          # never dereferenced
+    f = lib.kdt_tree_verify_attn_noalloc
+    f.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    assert f(*([fake] * 8), ctypes.c_float(1.0), fake, None, None, None) == _lib.KDT_ERR_INVALID_ARG
+    assert b"desc" in lib.kdt_last_error()

@@ -23,7 +23,7 @@ EXPORTS = [
     "kdt_build_visibility", "kdt_tree_verify_workspace_size", "kdt_tree_verify_attn",
     "kdt_tree_verify_plan", "kdt_tree_verify_prepare", "kdt_tree_verify_attend", "kdt_tree_verify_combine",
     "kdt_tree_verify_num_splits", "kdt_status_string", "kdt_last_error", "kdt_last_status", "kdt_version",
-    "kdt_tree_accept", "kdt_kv_compact", "kdt_build_tree",
+    "kdt_tree_accept", "kdt_kv_compact", "kdt_build_tree", "kdt_tree_verify_attn_noalloc",
 ]
 
 
@@ -286,3 +286,27 @@ def kv_compact(ckv, krope, cache_lens, tree_ckv, tree_krope, path, accept_len, d
                                  int(capacity_rows), ctypes.byref(desc), _ptr(dev_status), _stream(stream)))
     return new_lens
 
+
+# ---------------------------------------------------------------- allocation-free variant
+def _load_noalloc():
+    lib = load()
+    f = lib.kdt_tree_verify_attn_noalloc
+    if f.argtypes is None:
+        f.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_float, ctypes.c_void_p, ctypes.POINTER(VerifyDesc),
+                                              ctypes.c_void_p, ctypes.c_void_p]
+        f.restype = ctypes.c_int
+    return f
+
+
+def tree_verify_attn_noalloc(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, bitmask, cache_lens, scale: float, *,
+                             max_cache_len: int, out, dev_status=None, total_cache_len: Optional[int] = None,
+                             desc: Optional[VerifyDesc] = None, stream=None) -> torch.Tensor:
+    """kdt_tree_verify_attn_noalloc (include/kdt_noalloc.h): the verify attention with the
+    library's static per-device scratch array as its workspace.  `out` must be given (nothing is
+    allocated); returns it."""
+    if desc is None:
+        desc = make_desc(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, max_cache_len, total_cache_len)
+    _check(_load_noalloc()(
+        _ptr(q_lat), _ptr(q_rope), _ptr(ckv), _ptr(krope), _ptr(tree_ckv), _ptr(tree_krope), _ptr(bitmask),
+        _ptr(cache_lens), ctypes.c_float(scale), _ptr(out), ctypes.byref(desc), _ptr(dev_status), _stream(stream)))
+    return out
