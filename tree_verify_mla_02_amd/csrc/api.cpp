@@ -193,7 +193,12 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     // (56.8 vs 60.5 us there; 16 x 2 blocks: 57.7 us).
     x.bs = (S >= 4 && rt >= 16) ? 4 : 1;
     x.bt = (int)(x.bs > 1 ? (rt + 3) / 4 : rt);
-    x.groups = (int64_t)d.batch * ((rt + x.bt - 1) / x.bt) * ((S + x.bs - 1) / x.bs);
+    // A group runs on one XCD, so fewer groups than XCDs would leave XCDs idle (one request
+    // of 128 row tiles with 2 splits would run on 2 of the 8): halve the row-tile blocks until
+    // every XCD has a group.
+    auto ngroups = [&]() { return (int64_t)d.batch * ((rt + x.bt - 1) / x.bt) * ((S + x.bs - 1) / x.bs); };
+    while (ngroups() < kXcds && x.bt > 1) x.bt = (x.bt + 1) / 2;
+    x.groups = ngroups();
     const int64_t groups = x.groups;
     x.units = (groups + 7) / 8 * 8 * ((int64_t)x.bt * x.bs);
     if (x.units > INT32_MAX) return false;

@@ -25,6 +25,7 @@ constexpr int kMaxNodes = 256;                         // 4 mask words
 constexpr int kMinChunk = KDT_MIN_CHUNK;               // keys per split at least (a multiple of 64)
 static_assert(kMinChunk % 64 == 0 && kMinChunk >= 64, "whole key tiles per split");
 constexpr int kMaxTreeTable = 8192;                    // tree builder: D * K log probabilities in LDS
+constexpr int kXcds = 8;                               // MI355X: 8 XCDs, each with its own L2
 
 struct Geometry {
     int64_t rows;          // R = N * H query rows per request

@@ -71,7 +71,6 @@ __device__ __forceinline__ int splits_of(int L, int64_t chunk, int S) {
 // a single XCD x: its key tiles come from HBM once and from that L2 for the other row tiles.
 // Groups are sorted by work (keys), dealt to XCDs in snake order (0..7, 7..0, ...) to balance
 // the XCDs, and each XCD runs its groups longest first.
-constexpr int kXcds = 8;
 constexpr int kMaxSortGroups = 2048;    // above this the groups keep request order
 
 // Division of 32-bit unsigned integers by a divisor d (1 <= d <= 2^31) fixed for the launch, as
@@ -302,10 +301,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs pa) {
 template <int W>
 __global__ __launch_bounds__(256) void prepare_kernel(const int32_t *__restrict__ parents,
                                                       uint64_t *__restrict__ masks, PlanArgs pa) {
-    __shared__ int32_t par[kMaxNodes];
+    __shared__ VisLds vis;
     __shared__ PlanLds lds;
     if ((int)blockIdx.x < pa.B)
-        visibility_rows<W>(parents, pa.N, masks, pa.dev_status, blockIdx.x, par);
+        visibility_rows<W>(parents, pa.N, masks, pa.dev_status, blockIdx.x, vis);   // 256 threads >= N
     else
         plan_body(pa, lds);
 }

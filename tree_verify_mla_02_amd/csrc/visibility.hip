@@ -1,5 +1,5 @@
-// Ancestor bitmasks of draft trees: the standalone launch, one workgroup per request
-// (the walk and its citation are in visibility_rows.h).
+// Ancestor bitmasks of draft trees: the standalone launch, one workgroup per request of
+// ceil(N/64) waves (the builder and its citation are in visibility_rows.h).
 #include "visibility_rows.h"
 
 namespace kdt {
@@ -8,8 +8,8 @@ template <int W>
 __global__ __launch_bounds__(256) void visibility_kernel(const int32_t *__restrict__ parents, int N,
                                                          uint64_t *__restrict__ masks,
                                                          int32_t *__restrict__ dev_status) {
-    __shared__ int32_t par[kMaxNodes];
-    visibility_rows<W>(parents, N, masks, dev_status, blockIdx.x, par);
+    __shared__ VisLds lds;
+    visibility_rows<W>(parents, N, masks, dev_status, blockIdx.x, lds);
 }
 
 hipError_t launch_visibility(const int32_t *parents, int B, int N, uint64_t *masks,
