@@ -788,26 +788,28 @@ __device__ __forceinline__ void pv_pair(const LDS_AS char *buf, const u32x4 (&ph
 }
 
 // Split partials of bf16 requests are stored as 24-bit floats: the top 24 bits of the fp32
-// value (sign, exponent, 15 mantissa bits) rounded to nearest even -- relative error <= 2^-16,
-// far inside the 2e-3 output tolerance -- 4 values in 3 words, so the partial round trip
-// through memory (the cost of splitting keys over workgroups) is a quarter smaller.  fp32
-// requests keep plain fp32 partials: 2^-16 of an output of magnitude 1 is already above their
-// 1e-5 tolerance.
-__device__ __forceinline__ uint32_t to24(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7fu + ((u >> 8) & 1u)) >> 8;
-}
-__device__ __forceinline__ float from24(uint32_t v) { return __uint_as_float(v << 8); }
+// value (sign, exponent, 15 mantissa bits), the magnitude rounded half away from zero by adding
+// 0x80 before the low byte is dropped -- relative error <= 2^-16, far inside the 2e-3 output
+// tolerance -- 4 values in 3 words, so the partial round trip through memory (the cost of
+// splitting keys over workgroups) is a quarter smaller.  Packing is one add per value and one
+// v_perm_b32 byte select per word; unpacking one byte select per value.  fp32 requests keep
+// plain fp32 partials: 2^-16 of an output of magnitude 1 is already above their 1e-5 tolerance.
+// (A finite value cannot carry into infinity: that needs a magnitude above 3.4e38.)
 __device__ __forceinline__ void pack24x4(uint32_t *dst, float a, float b, float c, float d) {
-    const uint32_t x = to24(a), y = to24(b), z = to24(c), w = to24(d);
-    dst[0] = x | (y << 24);
-    dst[1] = (y >> 8) | (z << 16);
-    dst[2] = (z >> 16) | (w << 8);
+    const uint32_t x = __float_as_uint(a) + 0x80u, y = __float_as_uint(b) + 0x80u;
+    const uint32_t z = __float_as_uint(c) + 0x80u, w = __float_as_uint(d) + 0x80u;
+    // __builtin_amdgcn_perm(hi, lo, sel): byte k of the result is byte sel_k of the 8-byte value
+    // hi:lo (0-3 from lo, 4-7 from hi; 12 gives 0)
+    dst[0] = __builtin_amdgcn_perm(y, x, 0x05030201u);      // x1 x2 x3 y1
+    dst[1] = __builtin_amdgcn_perm(z, y, 0x06050302u);      // y2 y3 z1 z2
+    dst[2] = __builtin_amdgcn_perm(w, z, 0x07060503u);      // z3 w1 w2 w3
 }
 __device__ __forceinline__ float4 unpack24x4(const uint32_t *src) {
     const uint32_t p = src[0], q = src[1], r = src[2];
-    return make_float4(from24(p & 0xffffffu), from24((p >> 24) | ((q & 0xffffu) << 8)),
-                       from24((q >> 16) | ((r & 0xffu) << 16)), from24(r >> 8));
+    return make_float4(__uint_as_float(__builtin_amdgcn_perm(0u, p, 0x0201000Cu)),    // 0 x1 x2 x3
+                       __uint_as_float(__builtin_amdgcn_perm(q, p, 0x0504030Cu)),     // 0 y1 y2 y3
+                       __uint_as_float(__builtin_amdgcn_perm(r, q, 0x0403020Cu)),     // 0 z1 z2 z3
+                       __uint_as_float(__builtin_amdgcn_perm(0u, r, 0x0302010Cu)));   // 0 w1 w2 w3
 }
 
 // Store / load of 4 partial values in the format of the input type: kPartWords<T> words each.
