@@ -448,11 +448,20 @@ __device__ __forceinline__ void rescale_acc(f32x16 (&o)[NT], float alpha) {
 
 // ------------------------------------------------------------------------------ softmax
 // Online softmax of one query row over 32-key blocks, in base 2 (scores times scale*log2 e).
-// Probabilities are taken relative to a reference max m_ref that moves only when the row
-// max exceeds it by more than kLazy: O and l are then rescaled (rare).  Otherwise P stays
-// below 2^kLazy, which fp32 and the bf16 hi/lo pair represent with the same relative
-// accuracy as P <= 1, so the result is the same softmax without a rescale per tile.
-constexpr float kLazy = 8.f;
+// Probabilities are taken relative to a reference m_ref rather than the running max m_max: P
+// may exceed 1, and fp32 and the bf16 hi/lo pair keep the same relative accuracy at any
+// magnitude, so the result is the same softmax.  The reference moves only when a block max
+// passes it by more than kLazy; O and l are then rescaled by 2^(old - new) -- for the whole
+// wave, since each lane holds its row's accumulator, whichever of the 32 rows needed it.  So
+// when one row must move, every row of the wave moves, to its own running max + kHead: the
+// rescale is paid once for all, and a row next forces one only when its max has risen by more
+// than kHead + kLazy.  On inputs with large outliers (scores spread over hundreds, base 2)
+// this cuts wave rescales from a quarter of the 32-key blocks to a few percent.
+// Bounds: P <= 2^kLazy and, for the row's running max, P >= 2^-kHead, so keys more than
+// 126 - kHead below the max underflow (weight below 2^-94: nothing); O <= keys * 2^kLazy * max|v|
+// stays finite for latent magnitudes below 2^60.
+constexpr float kLazy = 32.f;
+constexpr float kHead = 32.f;
 
 struct Update {
     float m_use;    // reference the block's probabilities are taken against (0 if none yet)
@@ -491,17 +500,22 @@ __device__ __forceinline__ void mask_scores(f32x16 &s, uint32_t w) {
 // c = scale * log2(e) is made positive once per workgroup (see normalise_scale), so the row
 // max of the raw scores gives the max of the scaled ones and -inf scores map to P = 0.
 struct SoftmaxRow {
-    float m_ref;    // reference max (base-2 domain), -inf until the row sees a key
+    float m_ref;    // reference (base-2 domain), -inf until the row sees a key
+    float m_max;    // running max of the row's scaled scores, -inf until it sees a key
     float l;        // running sum of probabilities relative to m_ref (this lane's keys only)
     float c;        // scale * log2(e), > 0
 
+    // Called by every lane of the wave together (the move decision is a wave ballot).
     __device__ __forceinline__ Update update_from_max(float e) {
-        const float mx = e * c;                                // -inf stays -inf
-        const bool upd = mx > m_ref + kLazy;                   // also true for the first visible key
-        const float m_new = upd ? mx : m_ref;
+        const float bm = e * c;                                // -inf stays -inf
+        const float mm = fmaxf(m_max, bm);
+        // also true for the first visible key (m_ref = -inf); -inf stays -inf
+        const bool any = __ballot(bm > m_ref + kLazy) != 0;
+        const float m_new = any ? mm + kHead : m_ref;
         // exponent 0 (alpha = 1) unless an existing reference moves; no branch
-        const float alpha = __builtin_amdgcn_exp2f((upd && m_ref != -INFINITY) ? m_ref - m_new : 0.f);
+        const float alpha = __builtin_amdgcn_exp2f((m_new != m_ref && m_ref != -INFINITY) ? m_ref - m_new : 0.f);
         m_ref = m_new;
+        m_max = mm;
         return Update{m_new == -INFINITY ? 0.f : m_new, alpha};
     }
 
@@ -544,10 +558,10 @@ struct SoftmaxRow {
 // each MFMA.  A wave issues in order and an MFMA holds the issue port for about half of its 32
 // cycles, so only work placed between two MFMAs runs in the matrix core's shadow: a larger
 // group stalls the next MFMA.  Steps: partial maxima (4), cross-lane max and reference update
-// (3), then per pair of probabilities (8 pairs) exp2, sum, and the exact split into bf16 hi +
+// (4), then per pair of probabilities (8 pairs) exp2, sum, and the exact split into bf16 hi +
 // lo (4 each): p = hi + lo_exact with hi = bf16(p) (round to nearest) and lo_exact = p - hi
 // exact in fp32, then lo = bf16(lo_exact).
-constexpr int kSmPre = 7;
+constexpr int kSmPre = 8;
 constexpr int kSmStages = kSmPre + 8 * 4;
 __device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 // Empty asm that takes a value as an in/out operand: the value must be computed at this point
@@ -559,7 +573,8 @@ __device__ __forceinline__ void pin(V &x) { asm volatile("" : "+v"(x)); }
 struct BlockSm {
     f32x16 s;          // raw scores (masked keys -inf)
     float m0, m1, m2, m3, m4;   // partial maxima
-    float mx;          // new reference candidate
+    float bm, mm, thr; // block max, new running max, move threshold
+    float mx;          // new reference
     float sum;         // sum of this lane's probabilities
     Update u;
     float x1, p0, p1, h0f;
@@ -587,18 +602,23 @@ struct BlockSm {
             m0 = row_max(m0);
             pin(m0);
         } else if constexpr (ST == 5) {
-            // the reference moves when the block max passes it by more than kLazy (also for
-            // the first visible key); -inf stays -inf
-            const float m = m0 * sm.c;
-            mx = m > sm.m_ref + kLazy ? m : sm.m_ref;
-            pin(mx);
+            bm = m0 * sm.c;
+            mm = fmaxf(sm.m_max, bm);
+            thr = sm.m_ref + kLazy;
+            pin(bm), pin(mm), pin(thr);
         } else if constexpr (ST == 6) {
+            // every row of the wave moves when some row's block max passes its reference by
+            // more than kLazy (also for the first visible key); -inf stays -inf
+            mx = __ballot(bm > thr) != 0 ? mm + kHead : sm.m_ref;
+            pin(mx);
+        } else if constexpr (ST == 7) {
             // alpha = 1 unless an existing reference moves; no branch
             u.alpha = __builtin_amdgcn_exp2f((mx != sm.m_ref && sm.m_ref != -INFINITY) ? sm.m_ref - mx : 0.f);
             sm.m_ref = mx;
+            sm.m_max = mm;
             u.m_use = mx == -INFINITY ? 0.f : mx;
             sum = 0.f;
-            pin(u.alpha), pin(u.m_use), pin(sm.m_ref), pin(sum);
+            pin(u.alpha), pin(u.m_use), pin(sm.m_ref), pin(sm.m_max), pin(sum);
         } else if constexpr (ST < kSmStages) {
             constexpr int k = (ST - kSmPre) / 4, r = (ST - kSmPre) % 4;
             if constexpr (r == 0) {
@@ -954,7 +974,7 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     f32x16 o[NT16];
 #pragma unroll
     for (int t = 0; t < NT16; t++) o[t] = (f32x16){};
-    SoftmaxRow sm{-INFINITY, 0.f, c_pos};
+    SoftmaxRow sm{-INFINITY, -INFINITY, 0.f, c_pos};
 
     for (int t = 0; t < n_tiles; t++) {
         wait_vm_all();
@@ -1304,7 +1324,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     f32x16 o[NT16];
 #pragma unroll
     for (int t = 0; t < NT16; t++) o[t] = (f32x16){};
-    SoftmaxRow sm{-INFINITY, 0.f, c_pos};
+    SoftmaxRow sm{-INFINITY, -INFINITY, 0.f, c_pos};
 
     for (int t = 0; t < n_tiles; t++) {
         wait_vm_all();
