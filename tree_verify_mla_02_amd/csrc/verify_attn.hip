@@ -1186,18 +1186,23 @@ __device__ __forceinline__ void qk_block(const LDS_AS char *const (&pq)[Sh::CB /
 }
 
 // O^T += V^T P^T over one 32-key block: 2 x 16-key steps x NT16 column tiles x (hi, lo) = 4*NT16
-// MFMAs; vbuf already points at the wave's block.  fill(m) runs after MFMA m.
+// MFMAs; vbuf already points at the wave's block.  fill(m) runs after MFMA m.  The column tiles
+// are taken rotated by NT16/2 when `rot` is the byte distance between column tiles 0 and NT16/2
+// (0: not rotated): accumulator t then holds column tile (t + NT16/2) % NT16.
 template <class Sh, int NT16, class F>
-__device__ __forceinline__ void pv_block(const LDS_AS char *vbuf, const u32x4 (&phi)[2], const u32x4 (&plo)[2],
-                                         f32x16 (&o)[NT16], const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1][2],
-                                         F &&fill) {
+__device__ __forceinline__ void pv_block(const LDS_AS char *vbuf, int rot, const u32x4 (&phi)[2],
+                                         const u32x4 (&plo)[2], f32x16 (&o)[NT16],
+                                         const int (&pv_base)[Sh::CB >= 8 ? Sh::CB / 4 : 1][2], F &&fill) {
     constexpr int NSTEP = 2 * NT16;     // (h16, t16) pairs
     constexpr int PD = 4;
+    static_assert((2 * NT16) % Sh::CB == 0, "half the column tiles are whole chunk groups");
+    const LDS_AS char *vlo = vbuf + rot, *vhi = vbuf - rot;
     auto load = [&](int st) {
         const int h16 = st / NT16, t16 = st % NT16;
         const int j = (4 * t16 % Sh::CB) / 4, cg_off = (4 * t16 / Sh::CB) * 1024 + key_off<Sh>(16 * h16);
-        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vbuf + pv_base[j][0] + cg_off));
-        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vbuf + pv_base[j][1] + cg_off));
+        const LDS_AS char *vb = t16 < NT16 / 2 ? vlo : vhi;
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vb + pv_base[j][0] + cg_off));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4 *)(vb + pv_base[j][1] + cg_off));
         return (bf16x8)__builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     bf16x8 vf[PD];
@@ -1303,6 +1308,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
             for (int e = 0; e < 2; e++) pv_base[j][e] = lds_off<Sh>(w + 8 * e, 4 * j + y) + 8 * (lane & 1);
     }
     const int blk_off = kh * key_off<Sh>(32);          // this wave's 32-key block inside a tile
+    // key half 1 takes its column tiles rotated by NT16/2 (see the epilogue)
+    const int rot = kh * (2 * NT16 / Sh::CB) * 1024;
 
     bf16x8 q[NQ];
     wait_vm_all();
@@ -1365,7 +1372,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
         if (__ballot(bs.u.alpha != 1.f)) rescale_acc<NT16>(o, bs.u.alpha);
         constexpr int NC = Dma::NINST;
         static_assert(2 * (kSmStages - H1) <= 2 * NT16 && 2 * NC <= 4 * NT16, "steps fit in the chain");
-        pv_block<Sh, NT16>(buf + blk_off, bs.phi, bs.plo, o, pv_base, [&](auto M) {
+        pv_block<Sh, NT16>(buf + blk_off, rot, bs.phi, bs.plo, o, pv_base, [&](auto M) {
             constexpr int m = decltype(M)::value;
             if constexpr (m % 2 == 1 && H1 + m / 2 < kSmStages) bs.template stage<H1 + m / 2>(sm);
             if constexpr (m % 2 == 0 && m / 2 < NC) dn.template issue<m / 2, m / 2 + 1>();
@@ -1375,68 +1382,75 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     wait_vm_all();                       // no copy may still be landing
     __syncthreads();                     // every wave is done with the tile buffers
 
-    // ---- merge the two key halves of each row half: waves kh = 1 hand (m, l, O) over
-    float m_run = sm.m_ref, l_run = sm.l;
-    // [rh][t16][g][lane] float4: each store and load moves 16 contiguous bytes per lane
+    // ---- merge the two key halves of each row half.  Wave (rh, kh) accumulated its column tiles
+    // rotated by kh * NT16/2: o[0 .. HT) are column tiles kh*HT .. +HT-1, its own half of the
+    // output, and o[HT .. NT16) the other wave's half.  Each wave hands that other half and its
+    // (m, l) over through LDS, merges its own half, and writes it: all four waves share the
+    // epilogue, with register indices fixed at compile time.
+    constexpr int HT = NT16 / 2;
+    // [rh][sender kh][t][g][lane] float4: each store and load moves 16 contiguous bytes per lane
     float4 *xo = (float4 *)smem;
-    float2 *xml = (float2 *)((char *)smem + 2 * 64 * 16 * NT16 * 4);  // [rh][64]
-    if (kh == 1) {
+    float2 *xml = (float2 *)((char *)smem + 2 * 2 * HT * 4 * 64 * 16);     // [rh][kh][64]
+    static_assert(2 * 2 * HT * 4 * 64 * 16 + 2 * 2 * 64 * 8 <= 2 * Sh::TILE_BYTES, "exchange fits in the tiles");
 #pragma unroll
-        for (int t16 = 0; t16 < NT16; t16++)
+    for (int t = 0; t < HT; t++)
 #pragma unroll
-            for (int g = 0; g < 4; g++)
-                xo[((rh * NT16 + t16) * 4 + g) * 64 + lane] =
-                    make_float4(o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2], o[t16][4 * g + 3]);
-        xml[rh * 64 + lane] = make_float2(m_run, l_run);
-    }
+        for (int g = 0; g < 4; g++)
+            xo[(((rh * 2 + kh) * HT + t) * 4 + g) * 64 + lane] =
+                make_float4(o[HT + t][4 * g], o[HT + t][4 * g + 1], o[HT + t][4 * g + 2], o[HT + t][4 * g + 3]);
+    xml[(rh * 2 + kh) * 64 + lane] = make_float2(sm.m_ref, sm.l);
     __syncthreads();
-    if (kh == 1) return;
+    float m_run, l_run;
     {
-        const float2 ml1 = xml[rh * 64 + lane];
-        const float M = fmaxf(m_run, ml1.x);
-        const float c0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+        // (m, l) of key halves 0 and 1 in that order in both waves, so both get the same bits
+        const float2 ml0 = xml[(rh * 2 + 0) * 64 + lane], ml1 = xml[(rh * 2 + 1) * 64 + lane];
+        const float M = fmaxf(ml0.x, ml1.x);
+        const float c0 = ml0.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml0.x - M);
         const float c1 = ml1.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml1.x - M);
-        l_run = l_run * c0 + ml1.y * c1;
+        l_run = ml0.y * c0 + ml1.y * c1;
+        m_run = M;
+        const float cs = kh ? c1 : c0, cp = kh ? c0 : c1;       // own half, other half
+        const int pk = kh ^ 1;
 #pragma unroll
-        for (int t16 = 0; t16 < NT16; t16++)
+        for (int t = 0; t < HT; t++)
 #pragma unroll
             for (int g = 0; g < 4; g++) {
-                const float4 x = xo[((rh * NT16 + t16) * 4 + g) * 64 + lane];
-                o[t16][4 * g] = o[t16][4 * g] * c0 + x.x * c1;
-                o[t16][4 * g + 1] = o[t16][4 * g + 1] * c0 + x.y * c1;
-                o[t16][4 * g + 2] = o[t16][4 * g + 2] * c0 + x.z * c1;
-                o[t16][4 * g + 3] = o[t16][4 * g + 3] * c0 + x.w * c1;
+                const float4 x = xo[(((rh * 2 + pk) * HT + t) * 4 + g) * 64 + lane];
+                o[t][4 * g] = o[t][4 * g] * cs + x.x * cp;
+                o[t][4 * g + 1] = o[t][4 * g + 1] * cs + x.y * cp;
+                o[t][4 * g + 2] = o[t][4 * g + 2] * cs + x.z * cp;
+                o[t][4 * g + 3] = o[t][4 * g + 3] * cs + x.w * cp;
             }
-        m_run = M;
     }
 
-    // ---- epilogue, as the 128-row kernel's wave rh: lane holds O^T[t16*32 + (i/4)*8 + 4*half + i%4][row]
+    // ---- epilogue of the own half, as the 128-row kernel's wave rh for column tiles
+    // kh*HT .. +HT-1: lane holds O^T[(kh*HT + t)*32 + (i/4)*8 + 4*half + i%4][row]
     const float l_tot = row_sum(l_run);
     if (!row_ok) return;
     if (sb == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float *dst = a.out + ((int64_t)b * R + r) * DC;
+        float *dst = a.out + ((int64_t)b * R + r) * DC + kh * HT * 32;
 #pragma unroll
-        for (int t16 = 0; t16 < NT16; t16++)
+        for (int t = 0; t < HT; t++)
 #pragma unroll
             for (int g = 0; g < 4; g++) {
-                const float4 v = make_float4(o[t16][4 * g] * inv, o[t16][4 * g + 1] * inv, o[t16][4 * g + 2] * inv,
-                                             o[t16][4 * g + 3] * inv);
-                *(float4 *)(dst + t16 * 32 + g * 8 + 4 * half) = v;
+                const float4 v = make_float4(o[t][4 * g] * inv, o[t][4 * g + 1] * inv, o[t][4 * g + 2] * inv,
+                                             o[t][4 * g + 3] * inv);
+                *(float4 *)(dst + t * 32 + g * 8 + 4 * half) = v;
             }
     } else {
         const int64_t prow = ((int64_t)b * a.S + s) * R + r;
         // 32-row group 2*rt64 + rh of the request = group (rt64 & 1)*2 + rh of 128-row tile rt64/2
         const int64_t blk = (((int64_t)b * a.S + s) * a.RT + (rt64 >> 1)) * kWaves + (rt64 & 1) * 2 + rh;
         constexpr int PW = kPartWords<T>;
-        uint32_t *dst = a.part_o + blk * (kRowsPerWave * DC / 4 * PW) + lane * PW;
+        uint32_t *dst = a.part_o + blk * (kRowsPerWave * DC / 4 * PW) + lane * PW + kh * HT * 4 * 64 * PW;
 #pragma unroll
-        for (int t16 = 0; t16 < NT16; t16++)
+        for (int t = 0; t < HT; t++)
 #pragma unroll
             for (int g = 0; g < 4; g++)
-                store_part4<T>(dst + (t16 * 4 + g) * 64 * PW, o[t16][4 * g], o[t16][4 * g + 1], o[t16][4 * g + 2],
-                               o[t16][4 * g + 3]);
-        if (half == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
+                store_part4<T>(dst + (t * 4 + g) * 64 * PW, o[t][4 * g], o[t][4 * g + 1], o[t][4 * g + 2],
+                               o[t][4 * g + 3]);
+        if (half == 0 && kh == 0) a.part_ml[prow] = make_float2(m_run, l_tot);
     }
 }
 
