@@ -87,9 +87,19 @@ SMALL = {
                     None),
     # small requests in a batch that fills the GPU: 128-row workgroups, no split
     "batch300": (workloads.Spec("b300", 65, 300, 2, 64, 512, 64, "bf16", None, ragged=(1, 300), tree="random"), None),
-    # 1000 rows: 128-row workgroups with a partial last tile, two mask words, a split
+    # 1000 rows over short caches: 64-row workgroups (16 row tiles, the last partial), two mask
+    # words, a split
     "rows1000": (workloads.Spec("r1000", 66, 2, 125, 8, 512, 64, "bf16", None, ragged=(700, 2600), depth=10, topk=6),
                  None),
+    # the same rows over a long cache: 128-row workgroups with a partial last tile
+    "rows1000_long": (workloads.Spec("r1000l", 67, 1, 125, 8, 512, 64, "bf16", 9000, depth=10, topk=6), None),
+    # mid-size trees over short ragged caches (64-row workgroups beyond 512 rows): 2560 rows a
+    # request, an empty cache and a one-key tail; 888 rows (a partial 64-row tile, H = 24 so
+    # 32-row slices straddle nodes), outliers
+    "t64_ragged": (workloads.Spec("t64r", 72, 3, 40, 64, 512, 64, "bf16", None, ragged=(0, 3000), depth=8, topk=8),
+                   [0, 1, 2999]),
+    "t64_rows888": (workloads.Spec("t64p", 73, 2, 37, 24, 512, 64, "bf16", None, ragged=(100, 5000), tree="random",
+                                   outlier_p=0.01), [5000, 777]),
 }
 
 
@@ -244,8 +254,8 @@ def test_abi_errors_on_device():
 @pytest.mark.parametrize("seed", range(4))
 def test_random_small_requests(seed):
     """Random small batches (at most 512 rows per request, so they take 64-row workgroups when the
-    batch is small, 128-row ones otherwise): random trees, heads, ragged lengths with empty
-    caches and one-key tails, all rows against the oracle."""
+    batch does not fill the GPU, 128-row ones otherwise): random trees, heads, ragged lengths
+    with empty caches and one-key tails, all rows against the oracle."""
     rng = np.random.default_rng(1000 + seed)
     for case in range(4):
         B = int(rng.integers(1, 7))

@@ -153,11 +153,17 @@ int set_error(int code, const char *msg) { return fail(code, "%s", msg); }
 bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     Geometry x{};
     x.rows = (int64_t)d.num_nodes * d.num_heads;
-    // Requests of at most 512 rows (a decode step, small trees) take 64-row workgroups when
-    // 128-row ones would not fill the GPU: twice the workgroups for the same keys, each wave
-    // working on one 32-key block of every tile (bf16, d = 512 + 64 only).
+    // 64-row workgroups (bf16, d = 512 + 64 only) when 128-row ones would not fill the GPU:
+    // twice the workgroups for the same keys, each wave working on one 32-key block of every
+    // tile.  For requests of at most 512 rows (a decode step, small trees) 128-row tiles would
+    // be half empty.  Larger requests (up to 8192 rows) take them over short caches (at most
+    // 8192 keys), where the key split that fills the GPU makes partials that are large next to
+    // the key work: halving the split count halves the partials written and merged, which
+    // outweighs the 64-row kernel's less efficient tile loop (the Kimi shape, 4096 rows over
+    // 4096 keys: 74.4 -> 71.0 us per step; over 32768 keys, the chain shape, it does not pay).
     const int64_t rt128 = (x.rows + kRowsPerTile - 1) / kRowsPerTile;
-    const bool small = d.dtype == KDT_BF16 && d.d_latent == 512 && d.d_rope == 64 && x.rows <= 512 &&
+    const bool small = d.dtype == KDT_BF16 && d.d_latent == 512 && d.d_rope == 64 &&
+                       (x.rows <= 512 || (x.rows <= 8192 && d.max_cache_len <= 8192)) &&
                        (int64_t)d.batch * rt128 < num_cus;
     x.tile_rows = small ? kRowsPerTile / 2 : kRowsPerTile;
     const int64_t rt = (x.rows + x.tile_rows - 1) / x.tile_rows;

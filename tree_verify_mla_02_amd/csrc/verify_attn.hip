@@ -1144,8 +1144,9 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------ 64-row workgroups
-// Small requests: a decode step (one node x up to 64 heads) or a small tree, at most 512 rows.
-// With the 128-row workgroup above a 64-row request would leave half of the rows empty, and
+// Requests that cannot fill the GPU with 128-row workgroups: a decode step (one node x up to 64
+// heads), a small tree, or a tree of up to 8192 rows over a short cache (the host's geometry
+// picks them).  With the 128-row workgroup above a 64-row request would leave half of the rows empty, and
 // every wave would still issue the 200 MFMAs of a 64-key tile: one CU's matrix pipes, not HBM,
 // would bound the key stream.  Here a workgroup takes 64 rows and wave w = (key half kh, row
 // half rh) takes rows 32*rh .. +31 and keys 32*kh .. +31 of every tile: 36 QK + 64 P.V MFMAs
