@@ -1483,32 +1483,49 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
     const int t16 = (int)((tile / NSUB) % NT16);
     const int64_t grp = (tile / (NSUB * NT16)) % groups;
     const int b = (int)(tile / (NSUB * NT16 * groups));
-    const int ok = a.hdr->ok;                         // both loads in flight together
-    const int sb = splits_of(a.lens[b], a.chunk, a.S);
-    if (!ok || sb <= 1) return;                       // uniform over the workgroup
     const int64_t r = grp * kRowsPerWave + (lane & 31);
     const bool valid = r < a.R;
     const int64_t rc = valid ? r : a.R - 1;
     const int rt = (int)(grp / kWaves), wave = (int)(grp % kWaves);
+    constexpr int U = 8;                              // splits in flight per wave
+    float2 ml[U];
+    float4 x[U][GC];
+    // The first U splits' loads go out before the plan's verdict and the request's split count
+    // arrive (splits the request does not have are read from the workspace and ignored): the
+    // merge waits for one memory round trip instead of two.
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const int sp = wv + u * WS;
+        if (sp < a.S) {
+            ml[u] = a.part_ml[((int64_t)b * a.S + sp) * a.R + rc];
+            const int64_t blk = (((int64_t)b * a.S + sp) * a.RT + rt) * kWaves + wave;
+            const uint32_t *src = a.part_o + blk * (kRowsPerWave * DC / 4 * PW) + lane * PW;
+#pragma unroll
+            for (int g = 0; g < GC; g++) x[u][g] = load_part4<F32P>(src + (t16 * 4 + sub * GC + g) * 64 * PW);
+        }
+    }
+    const int ok = a.hdr->ok;
+    const int sb = splits_of(a.lens[b], a.chunk, a.S);
+    if (!ok || sb <= 1) return;                       // uniform over the workgroup
     float acc[GC][4];
 #pragma unroll
     for (int g = 0; g < GC; g++)
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[g][j] = 0.f;
     float M = -INFINITY, den = 0.f;
-    constexpr int U = 8;                              // splits in flight per wave
     for (int s0 = wv; s0 < sb; s0 += U * WS) {
-        float2 ml[U];
-        float4 x[U][GC];
+        if (s0 != wv) {
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int sp = s0 + u * WS;
-            if (sp < sb) {
-                ml[u] = a.part_ml[((int64_t)b * a.S + sp) * a.R + rc];
-                const int64_t blk = (((int64_t)b * a.S + sp) * a.RT + rt) * kWaves + wave;
-                const uint32_t *src = a.part_o + blk * (kRowsPerWave * DC / 4 * PW) + lane * PW;
+            for (int u = 0; u < U; u++) {
+                const int sp = s0 + u * WS;
+                if (sp < sb) {
+                    ml[u] = a.part_ml[((int64_t)b * a.S + sp) * a.R + rc];
+                    const int64_t blk = (((int64_t)b * a.S + sp) * a.RT + rt) * kWaves + wave;
+                    const uint32_t *src = a.part_o + blk * (kRowsPerWave * DC / 4 * PW) + lane * PW;
 #pragma unroll
-                for (int g = 0; g < GC; g++) x[u][g] = load_part4<F32P>(src + (t16 * 4 + sub * GC + g) * 64 * PW);
+                    for (int g = 0; g < GC; g++)
+                        x[u][g] = load_part4<F32P>(src + (t16 * 4 + sub * GC + g) * 64 * PW);
+                }
             }
         }
 #pragma unroll
