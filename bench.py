@@ -1,7 +1,7 @@
 """Benchmark of the tree-verify MLA-absorb attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kimi] [--no-cpu-baseline]
-                    [--cold-steps C]
+                    [--cold-steps C] [--attn-event-every E]
 
 A step is one pass of the whole path over one synthetic batch already resident in HBM:
 ancestor bitmasks from the parent array and the ragged plan (one fused launch), the attention
@@ -9,9 +9,9 @@ kernel and the split combine.  The default workload is the Kimi/DeepSeekV3-shape
 latent 512 + rope 64, bf16, committed cache 4096 tokens, a 64-node best-first draft tree).
 
 One JSON line is printed.  `value` is algorithmic TFLOP/s of the whole step;
-`roofline` rates the attention kernel alone (HIP events around each of its launches in the
-timed region, on the stream it runs on, recorded without a system-scope cache fence so that
-timing does not add cache write-backs to the step) against the roof that binds it (bf16 MFMA peak, or
+`roofline` rates the attention kernel alone (HIP events around its launches in every E-th
+step of the timed region, on the stream it runs on, recorded without a system-scope cache
+fence so that timing does not add cache write-backs to the step) against the roof that binds it (bf16 MFMA peak, or
 HBM bandwidth when the algorithmic intensity is below the ridge point), with `traffic` the HBM
 bytes per launch from the committed rocprofv3 counter summary (null when the kernel sources
 changed since it was taken); `cpu_baseline` times the fp64 oracle on the host cores.
@@ -139,26 +139,39 @@ def run(args):
         kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
         kdt.combine(out, desc, ws, stream=stream)
 
-    for _ in range(max(args.warmup, 1)):
+    step()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise SystemExit(f"device status {int(status.item())} on the benchmark inputs")
+    # the outputs of a first step against the oracle before anything is timed: masks bit for
+    # bit, attention rows within the tolerance (every row up to ~40 GFLOP of oracle work, else
+    # one row of every 32-row group of every request plus random rows).  The warm-up comes after
+    # it: the GPU clock falls while the host runs the oracle, and from idle it takes some 50 ms
+    # of back-to-back steps to settle (the Kimi step runs about 10 % slower before that).
+    check = check_outputs(inp, masks, out)
+    for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise SystemExit(f"device status {int(status.item())} on the benchmark inputs")
-    # the outputs of the warm-up steps against the oracle before anything is timed: masks bit
-    # for bit, attention rows within the tolerance (every row up to ~40 GFLOP of oracle work,
-    # else one row of every 32-row group of every request plus random rows)
-    check = check_outputs(inp, masks, out)
 
-    # ---- timed region: K whole steps; the attention kernel's own launches are bracketed by
-    # events on the stream it runs on (the same stream as the rest of the step)
+    # ---- timed region: K whole steps; the attention launches of every E-th step are bracketed
+    # by events on the stream they run on (the same stream as the rest of the step).  Each
+    # recorded event is a command-processor round trip between two kernels (a few microseconds
+    # of a 60-microsecond step when every step records two), so they are recorded on a sample
+    # of the timed steps.
     he = HipEvents()
-    evs = [(he.create(), he.create()) for _ in range(args.steps)]
+    every = max(1, args.attn_event_every)
+    sampled = [i for i in range(args.steps) if i % every == 0]
+    evs = {i: (he.create(), he.create()) for i in sampled}
 
     def timed_step(i):
         kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
-        he.record(evs[i][0], stream)
+        if i in evs:
+            he.record(evs[i][0], stream)
         kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
-        he.record(evs[i][1], stream)
+        if i in evs:
+            he.record(evs[i][1], stream)
         kdt.combine(out, desc, ws, stream=stream)
 
     torch.cuda.synchronize()
@@ -172,7 +185,7 @@ def run(args):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     step_ms = he.elapsed_ms(ev0, ev1) / args.steps
-    attn_each = np.array([he.elapsed_ms(a, b) for a, b in evs])
+    attn_each = np.array([he.elapsed_ms(*evs[i]) for i in sampled])
     attn_ms = float(attn_each.mean())
 
     # ---- cold caches: before each of a few steps, write a 512 MiB scratch buffer (twice the
@@ -240,6 +253,7 @@ def run(args):
         "alg_gflop_per_step": round(flops / 1e9, 4),
         "alg_mbytes_per_step": round(nbytes / 1e6, 4),
         "attn_kernel_ms": round(attn_ms, 5),
+        "attn_kernel_samples": len(sampled),
         "attn_kernel_ms_p10_p50_p90": [round(float(np.percentile(attn_each, q)), 5) for q in (10, 50, 90)],
         "attn_kernel_cold_ms_median": round(cold_ms, 5) if cold else None,
         "step_cold_ms_median": round(cold_step_ms, 5) if cold_step else None,
@@ -771,8 +785,10 @@ def recorded_traffic(workload: str, kernel: str = "verify_attn"):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--attn-event-every", type=int, default=5,
+                    help="bracket the attention launch of every E-th timed step with events (1: every step)")
     ap.add_argument("--workload", default="kimi", choices=sorted(workloads.SPECS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
