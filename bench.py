@@ -801,6 +801,8 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (to scale HBM byte counters)")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.attn_event_every < 1:
+        ap.error("--steps and --attn-event-every must be >= 1 and --warmup >= 0")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X with no sharding "
               "(the design notes describe how it would shard); run it with --gpus 1.", file=sys.stderr)
