@@ -160,7 +160,7 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     // 8192 keys), where the key split that fills the GPU makes partials that are large next to
     // the key work: halving the split count halves the partials written and merged, which
     // outweighs the 64-row kernel's less efficient tile loop (the Kimi shape, 4096 rows over
-    // 4096 keys: 74.4 -> 71.0 us per step; over 32768 keys, the chain shape, it does not pay).
+    // 4096 keys: about 5 % less time per step; over 32768 keys, the chain shape, it does not pay).
     const int64_t rt128 = (x.rows + kRowsPerTile - 1) / kRowsPerTile;
     const bool small = d.dtype == KDT_BF16 && d.d_latent == 512 && d.d_rope == 64 &&
                        (x.rows <= 512 || (x.rows <= 8192 && d.max_cache_len <= 8192)) &&
