@@ -1,15 +1,18 @@
 """Benchmark of the tree-verify MLA-absorb attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kimi] [--no-cpu-baseline]
-                    [--cold-steps C] [--attn-event-every E]
+                    [--cold-steps C] [--attn-event-every E] [--staged]
 
 A step is one pass of the whole path over one synthetic batch already resident in HBM:
-ancestor bitmasks from the parent array and the ragged plan (one fused launch), the attention
-kernel and the split combine.  The default workload is the Kimi/DeepSeekV3-shape request (H = 64 heads,
-latent 512 + rope 64, bf16, committed cache 4096 tokens, a 64-node best-first draft tree).
+ancestor bitmasks from the parent array, the ragged plan, the attention and the split combine.
+For one request on 64-row tiles (the Kimi shape, decode, small trees) the masks and the plan
+are made inside the attention launch (kdt_tree_verify_prepare_attend): two launches per step;
+other shapes, and --staged, run masks + plan as a launch of their own.  The default workload is
+the Kimi/DeepSeekV3-shape request (H = 64 heads, latent 512 + rope 64, bf16, committed cache
+4096 tokens, a 64-node best-first draft tree).
 
 One JSON line is printed.  `value` is algorithmic TFLOP/s of the whole step;
-`roofline` rates the attention kernel alone (HIP events around its launches in every E-th
+`roofline` rates the attention launch alone (HIP events around its launches in every E-th
 step of the timed region, on the stream it runs on, recorded without a system-scope cache
 fence so that timing does not add cache write-backs to the step) against the roof that binds it (bf16 MFMA peak, or
 HBM bandwidth when the algorithmic intensity is below the ridge point), with `traffic` the HBM
@@ -133,10 +136,24 @@ def run(args):
     out = torch.empty((sp.batch, sp.nodes, sp.heads, dc), dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    # masks, plan and attention in one launch where the shape allows (one request on 64-row
+    # tiles), else prepare and attend; --staged times the three launches everywhere
+    one_launch = not getattr(args, "staged", False) and kdt.prepare_attend_launches(desc) == 1
+
+    def prep():
+        if not one_launch:
+            kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
+
+    def attend():
+        if one_launch:
+            kdt.prepare_attend(parents, lens, q_lat, q_rope, ckv, krope, tckv, tkrope, inp.scale, out, desc, ws,
+                               masks_out=masks, dev_status=status, stream=stream)
+        else:
+            kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
 
     def step():
-        kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
-        kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
+        prep()
+        attend()
         kdt.combine(out, desc, ws, stream=stream)
 
     step()
@@ -166,10 +183,10 @@ def run(args):
     evs = {i: (he.create(), he.create()) for i in sampled}
 
     def timed_step(i):
-        kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
+        prep()
         if i in evs:
             he.record(evs[i][0], stream)
-        kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
+        attend()
         if i in evs:
             he.record(evs[i][1], stream)
         kdt.combine(out, desc, ws, stream=stream)
@@ -198,9 +215,9 @@ def run(args):
             scratch.fill_(1)
             s0, a0, a1, s1 = he.create(), he.create(), he.create(), he.create()
             he.record(s0, stream)
-            kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
+            prep()
             he.record(a0, stream)
-            kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
+            attend()
             he.record(a1, stream)
             kdt.combine(out, desc, ws, stream=stream)
             he.record(s1, stream)
@@ -252,13 +269,17 @@ def run(args):
         "cache_gbps": round(cache_bytes / (step_ms * 1e-3) / 1e9, 2),
         "alg_gflop_per_step": round(flops / 1e9, 4),
         "alg_mbytes_per_step": round(nbytes / 1e6, 4),
+        # the attention launch: with one_launch it also makes the masks and the plan (no
+        # prepare launch in the step)
+        "launches_per_step": (2 if one_launch else 3) if kdt.num_splits(desc) > 1 else (1 if one_launch else 2),
+        "attn_launch": "masks + plan + attention" if one_launch else "attention",
         "attn_kernel_ms": round(attn_ms, 5),
         "attn_kernel_samples": len(sampled),
         "attn_kernel_ms_p10_p50_p90": [round(float(np.percentile(attn_each, q)), 5) for q in (10, 50, 90)],
         "attn_kernel_cold_ms_median": round(cold_ms, 5) if cold else None,
         "step_cold_ms_median": round(cold_step_ms, 5) if cold_step else None,
         # the binding roof's fraction over other regions: the attention launch with cold caches,
-        # and the whole step (prepare + attention + combine), hot and cold
+        # and the whole step (masks + plan, attention, combine), hot and cold
         "frac_attn_cold": frac(cold_ms),
         "frac_step_hot": frac(step_ms),
         "frac_step_cold": frac(cold_step_ms),
@@ -601,15 +622,21 @@ def run_step_row(args):
     kv_out = kv if in_place else torch.empty((cap, kv.shape[1]), dtype=kv.dtype, device=dev)
     status = torch.zeros(1, **i32)
     stream = torch.cuda.current_stream(dev)
+    one_launch = not getattr(args, "staged", False) and kdt.prepare_attend_launches(desc) == 1
 
     def step(rec=None):
         mark = (lambda k: rec(k)) if rec else (lambda k: None)
         mark(0)
         kdt.build_tree(d_lp, d_cand, N, parents, tokens, depth, rank, stream=stream)
         mark(1)
-        kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
+        if not one_launch:
+            kdt.prepare(parents, lens, desc, ws, masks_out=masks, dev_status=status, stream=stream)
         mark(2)
-        kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
+        if one_launch:
+            kdt.prepare_attend(parents, lens, q_lat, q_rope, ckv, krope, tckv, tkrope, inp.scale, out, desc, ws,
+                               masks_out=masks, dev_status=status, stream=stream)
+        else:
+            kdt.attend(q_lat, q_rope, ckv, krope, tckv, tkrope, masks, inp.scale, out, desc, ws, stream=stream)
         mark(3)
         kdt.combine(out, desc, ws, stream=stream)
         mark(4)
@@ -684,6 +711,7 @@ def run_step_row(args):
                    "cache_len": maxL, "splits": kdt.num_splits(desc),
                    "compaction": "in place" if in_place else "into a second buffer"},
         "stage_us": {n: round(v * 1e3, 2) for n, v in stage.items()},
+        "attend_stage": "masks + plan + attention (prepare_us is 0)" if one_launch else "attention",
         "accepted_tokens": int(w_acc.sum()), "attention_max_abs_err_sampled": err,
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit_r,
                      "frac": round(achieved / peak, 4), "traffic": None},
@@ -791,6 +819,9 @@ def main():
                     help="bracket the attention launch of every E-th timed step with events (1: every step)")
     ap.add_argument("--workload", default="kimi", choices=sorted(workloads.SPECS))
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--staged", action="store_true",
+                    help="time prepare, attend and combine as three launches also where one launch makes the "
+                         "masks, the plan and the attention")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="attention launches timed after flushing L2 and MALL (0 to skip)")

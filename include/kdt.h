@@ -178,6 +178,29 @@ int kdt_tree_verify_prepare(const int32_t *parents, uint64_t *bitmask, const int
                             int32_t *dev_status, void *stream);
 
 /*
+ * kdt_tree_verify_prepare_attend -- kdt_tree_verify_prepare followed by kdt_tree_verify_attend,
+ * with their arguments, checks and results (bitmask is written, the workspace holds the plan,
+ * out or the split partials hold the attention; kdt_tree_verify_combine follows as after
+ * kdt_tree_verify_attend), in one launch where the shape allows.  A verify step needs the
+ * visibility masks ("Validating the Native Engine", section "The Broader Context") and the ragged
+ * plan before its attention.  For a one-request batch on 64-row workgroups (a decode step, small
+ * trees, the Kimi-size tree over short caches; kdt_tree_verify_prepare_attend_launches() == 1)
+ * both are made inside the attention launch: each workgroup works out the unit the plan would
+ * give its grid slot from cache_lens[0]; workgroups with tree keys walk the root paths of their
+ * rows' nodes; one workgroup builds all masks for bitmask.  Other shapes run the two stages.
+ * Results are bit-identical to the staged calls (the workspace included); a caller that reuses
+ * one plan for every layer still uses the staged calls.
+ */
+int kdt_tree_verify_prepare_attend(const int32_t *parents, uint64_t *bitmask, const int32_t *cache_lens,
+                                   const void *q_lat, const void *q_rope, const void *ckv_cache,
+                                   const void *krope_cache, const void *tree_ckv, const void *tree_krope, float scale,
+                                   float *out, const kdt_verify_desc *desc, void *workspace, size_t workspace_bytes,
+                                   int32_t *dev_status, void *stream);
+/* Kernel launches kdt_tree_verify_prepare_attend makes for desc: 1 or 2; -1 when desc is invalid
+ * (see kdt_last_error()). */
+int kdt_tree_verify_prepare_attend_launches(const kdt_verify_desc *desc);
+
+/*
  * kdt_tree_accept -- greedy acceptance closing a verify pass.  Accepted tokens are committed
  * and rejected ones discarded, and the target's prediction at the final accepted node is the
  * bonus token ("The Capstone Validation", sections "Context and Motivation" and "What the

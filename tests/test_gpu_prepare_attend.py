@@ -1,0 +1,202 @@
+"""kdt_tree_verify_prepare_attend against the staged calls (prepare, then attend) it replaces,
+each followed by combine.
+
+For a one-request batch on 64-row workgroups the call works out the plan unit of every grid
+slot and the visibility masks inside the attention launch (one launch); every other shape runs
+the two stages.  Either way its results must be the staged results bit for bit: the masks, the
+outputs, the whole workspace (plan header, offsets, lengths, unit list, split partials) and the
+device status.  Both workspaces start zeroed, so bytes nobody writes compare equal too.  The
+staged path itself is held to the oracle by the parity tests; one one-launch case is also
+checked against the oracle here.  The masks are those of "Validating the Native Engine", section "The Broader
+Context"; each output row is the attention of its own root-to-node path ("The Capstone
+Validation", section "Context and Motivation")."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_verify_mla_02_amd as kdt
+import workloads
+from gpu_helpers import TOL, report, to_device
+
+pytestmark = pytest.mark.gpu
+
+S = workloads.Spec
+CASES = {
+    "kimi": ("kimi", 3),
+    "decode": ("decode", 3),
+    "block8": ("block8", 3),
+    # 256 nodes x 2 heads = 512 rows: four mask words, four tree tiles
+    "n256": (S("fn256", 81, 1, 256, 2, 512, 64, "bf16", 5000, tree="random"), 1),
+    # no committed keys: one split, only the tree
+    "L0": (S("fL0", 82, 1, 5, 64, 512, 64, "bf16", 0, tree="random"), 1),
+    # 40 row tiles, last split partly filled
+    "rows2560": (S("f2560", 83, 1, 40, 64, 512, 64, "bf16", None, ragged=(2999, 2999), tree="random"), 1),
+    # 8192 rows over 8192 keys: the largest request the 64-row geometry takes
+    "rows8192": (S("f8192", 84, 1, 128, 64, 512, 64, "bf16", 8192, depth=12, topk=8), 1),
+    # 48 heads: a wave's 32 rows span two nodes; 480 rows, so the last row half is past R
+    "h48": (S("fh48", 86, 1, 10, 48, 512, 64, "bf16", 3000, tree="random"), 1),
+    # 16 heads (< 32): every workgroup with tree keys builds all masks; a 32-node chain
+    "h16chain": (S("fh16", 87, 1, 32, 16, 512, 64, "bf16", 2000, tree="chain"), 1),
+}
+
+
+def _inputs(name):
+    spec, seed = CASES[name]
+    return workloads.make_inputs(spec, seed=seed)
+
+
+def _run(inp, dev, cache_lens, fused, max_len=None, total_len=None):
+    """(masks, out, workspace bytes, status) of one call sequence on zeroed buffers."""
+    maxL = int(inp.cache_lens.max()) if max_len is None else max_len
+    desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, maxL,
+                         inp.total_len if total_len is None else total_len)
+    ws = torch.zeros(kdt.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full(dev.q_lat.shape, float("nan"), dtype=torch.float32, device="cuda")
+    B, N = dev.parents.shape
+    masks = torch.full((B, N, (N + 63) // 64), -1, dtype=torch.int64, device="cuda")
+    if fused:
+        kdt.prepare_attend(dev.parents, cache_lens, dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv,
+                           dev.tree_krope, inp.scale, out, desc, ws, masks_out=masks, dev_status=status)
+    else:
+        kdt.prepare(dev.parents, cache_lens, desc, ws, masks_out=masks, dev_status=status)
+        kdt.attend(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, masks, inp.scale, out,
+                   desc, ws)
+    kdt.combine(out, desc, ws)
+    torch.cuda.synchronize()
+    return masks.cpu(), out.cpu(), ws.cpu(), int(status.item()), desc
+
+
+def _same(a, b, what):
+    assert a[0].shape == b[0].shape and torch.equal(a[0], b[0]), f"{what}: masks differ"
+    assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32)), f"{what}: outputs differ"
+    diff = (a[2] != b[2]).nonzero()
+    assert diff.numel() == 0, f"{what}: workspace differs at {diff[:8].flatten().tolist()}"
+    assert a[3] == b[3], f"{what}: status {a[3]} vs {b[3]}"
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_fused_equals_staged(name):
+    inp = _inputs(name)
+    dev = to_device(inp)
+    staged = _run(inp, dev, dev.cache_lens, fused=False)
+    assert kdt.prepare_attend_launches(staged[4]) == 1, f"{name} should take the one-launch path"
+    print(f"case {name}: splits {kdt.num_splits(staged[4])}", flush=True)
+    fused = _run(inp, dev, dev.cache_lens, fused=True)
+    _same(fused, staged, name)
+    assert fused[3] == 0
+    for _ in range(2):                          # repeated calls on reused buffers give the same bits
+        again = _run(inp, dev, dev.cache_lens, fused=True)
+        _same(again, fused, name + " (repeat)")
+
+
+def test_fused_against_oracle_kimi():
+    inp = _inputs("kimi")
+    dev = to_device(inp)
+    masks, out, _, status, _ = _run(inp, dev, dev.cache_lens, fused=True)
+    ref_masks, ref_out, _ = oracle.run(inp)
+    assert status == 0
+    assert np.array_equal(masks.numpy().view(np.uint64), ref_masks)
+    dc = inp.spec.d_latent
+    err = float(np.abs(out.double().numpy().reshape(-1, dc) - ref_out.reshape(-1, dc)).max())
+    report("kimi-fused", err, TOL["bf16"])
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("L", [0, 1, 63, 64, 65, 1000, 1024, 1025, 4095])
+def test_fused_shorter_cache(L):
+    """cache_lens[0] below the bound the geometry was made for: fewer splits, partial splits."""
+    inp = _inputs("kimi")
+    dev = to_device(inp)
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    staged = _run(inp, dev, lens, fused=False, max_len=4096)
+    fused = _run(inp, dev, lens, fused=True, max_len=4096)
+    _same(fused, staged, f"L={L}")
+
+
+@pytest.mark.parametrize("L", [4097, -1])
+def test_fused_rejected_cache_len(L):
+    """A length outside [0, max_cache_len]: KDT_DEV_CACHE_LEN, outputs untouched, masks still
+    written -- as the staged calls do."""
+    inp = _inputs("kimi")
+    dev = to_device(inp)
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    staged = _run(inp, dev, lens, fused=False, max_len=4096)
+    fused = _run(inp, dev, lens, fused=True, max_len=4096)
+    _same(fused, staged, f"L={L}")
+    assert fused[3] == 2                         # KDT_DEV_CACHE_LEN
+    assert torch.isnan(fused[1]).all()
+
+
+def test_fused_total_len_bound():
+    """cache_lens[0] above total_cache_len is rejected like a length above max_cache_len."""
+    inp = _inputs("block8")
+    dev = to_device(inp)
+    staged = _run(inp, dev, dev.cache_lens, fused=False, max_len=4096, total_len=4000)
+    fused = _run(inp, dev, dev.cache_lens, fused=True, max_len=4096, total_len=4000)
+    _same(fused, staged, "total bound")
+    assert fused[3] == 2
+
+
+def test_fused_bad_parent():
+    """A parent link outside [-1, j-1]: the rows whose path meets it get zero masks and
+    KDT_DEV_BAD_PARENT, as the staged masks do."""
+    inp = _inputs("kimi")
+    parents = inp.parents.clone()
+    parents[0, 9] = 40                          # not below 9
+    parents[0, 30] = -7
+    inp = workloads.Inputs(inp.spec, parents, inp.cache_lens, inp.q_lat, inp.q_rope, inp.kv_cache, inp.tree_kv,
+                           inp.scale)
+    dev = to_device(inp)
+    staged = _run(inp, dev, dev.cache_lens, fused=False)
+    fused = _run(inp, dev, dev.cache_lens, fused=True)
+    _same(fused, staged, "bad parent")
+    assert fused[3] == 1                         # KDT_DEV_BAD_PARENT
+    assert (fused[0][0, 9] == 0).all() and (fused[0][0, 30] == 0).all()
+
+
+@pytest.mark.parametrize("name", ["t64_ragged", "chain_short", "tiny"])
+def test_fused_other_shapes_run_the_stages(name):
+    """Shapes the one-launch path does not take (several requests, 128-row tiles, fp32) give
+    the staged results through the same call (two launches)."""
+    spec = {"t64_ragged": S("t64r", 72, 3, 40, 64, 512, 64, "bf16", None, ragged=(0, 3000)),
+            "chain_short": S("chs", 85, 1, 16, 64, 512, 64, "bf16", 32768, tree="chain"),
+            "tiny": "tiny"}[name]
+    inp = workloads.make_inputs(spec, seed=4)
+    dev = to_device(inp)
+    staged = _run(inp, dev, dev.cache_lens, fused=False)
+    assert kdt.prepare_attend_launches(staged[4]) == 2
+    fused = _run(inp, dev, dev.cache_lens, fused=True)
+    _same(fused, staged, name)
+
+
+def test_fused_in_graph():
+    """prepare_attend + combine captured in a graph and replayed, with eager work between replays."""
+    inp = _inputs("kimi")
+    dev = to_device(inp)
+    eager = _run(inp, dev, dev.cache_lens, fused=True)
+    desc = eager[4]
+    ws = torch.zeros(kdt.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.zeros(dev.q_lat.shape, dtype=torch.float32, device="cuda")
+    masks = torch.zeros_like(eager[0], device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            kdt.prepare_attend(dev.parents, dev.cache_lens, dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv,
+                               dev.tree_krope, inp.scale, out, desc, ws, masks_out=masks, dev_status=status)
+            kdt.combine(out, desc, ws)
+    torch.cuda.synchronize()
+    for k in range(3):
+        out.fill_(float("nan"))
+        masks.fill_(-1)
+        scratch = torch.randn(1 << 20, device="cuda") * 2.0
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"replay {k}: scratch {float(scratch.sum()):.3f}", flush=True)
+        assert torch.equal(out.cpu().view(torch.int32), eager[1].view(torch.int32)), f"replay {k}: outputs differ"
+        assert torch.equal(masks.cpu(), eager[0]), f"replay {k}: masks differ"
+    assert int(status.item()) == 0

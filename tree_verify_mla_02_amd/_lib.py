@@ -24,6 +24,7 @@ EXPORTS = [
     "kdt_tree_verify_plan", "kdt_tree_verify_prepare", "kdt_tree_verify_attend", "kdt_tree_verify_combine",
     "kdt_tree_verify_num_splits", "kdt_status_string", "kdt_last_error", "kdt_last_status", "kdt_version",
     "kdt_tree_accept", "kdt_kv_compact", "kdt_build_tree", "kdt_tree_verify_attn_noalloc",
+    "kdt_tree_verify_prepare_attend", "kdt_tree_verify_prepare_attend_launches",
 ]
 
 
@@ -66,6 +67,8 @@ def load() -> ctypes.CDLL:
     lib.kdt_tree_verify_prepare.argtypes = [vp, vp, vp, dp, vp, sz, vp, vp]
     lib.kdt_tree_verify_attend.argtypes = [vp] * 7 + [ctypes.c_float, vp, dp, vp, sz, vp]
     lib.kdt_tree_verify_combine.argtypes = [vp, dp, vp, sz, vp]
+    lib.kdt_tree_verify_prepare_attend.argtypes = [vp] * 9 + [ctypes.c_float, vp, dp, vp, sz, vp, vp]
+    lib.kdt_tree_verify_prepare_attend_launches.argtypes = [dp]
     lib.kdt_tree_accept.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp]
     lib.kdt_kv_compact.argtypes = [vp] * 10 + [i64, dp, vp, vp]
     lib.kdt_build_tree.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
@@ -223,6 +226,31 @@ def attend(q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, bitmask, scale, out,
 def combine(out, desc: VerifyDesc, workspace, stream=None):
     _check(load().kdt_tree_verify_combine(_ptr(out), ctypes.byref(desc), _ptr(workspace), workspace.numel(),
                                           _stream(stream)))
+
+
+def prepare_attend(parents, cache_lens, q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, scale, out,
+                   desc: VerifyDesc, workspace, masks_out: Optional[torch.Tensor] = None, dev_status=None,
+                   stream=None) -> torch.Tensor:
+    """prepare + attend in one call (one launch for one request on 64-row tiles); combine
+    follows as after attend.  Returns the masks [B, N, ceil(N/64)] (int64 view of uint64)."""
+    if parents.dtype != torch.int32 or not parents.is_contiguous() or parents.dim() != 2:
+        raise ValueError("parents must be a contiguous [B, N] int32 tensor")
+    B, N = parents.shape
+    if masks_out is None:
+        masks_out = torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device=parents.device)
+    _check(load().kdt_tree_verify_prepare_attend(
+        _ptr(parents), _ptr(masks_out), _ptr(cache_lens), _ptr(q_lat), _ptr(q_rope), _ptr(ckv), _ptr(krope),
+        _ptr(tree_ckv), _ptr(tree_krope), ctypes.c_float(scale), _ptr(out), ctypes.byref(desc), _ptr(workspace),
+        workspace.numel(), _ptr(dev_status), _stream(stream)))
+    return masks_out
+
+
+def prepare_attend_launches(desc: VerifyDesc) -> int:
+    """Kernel launches prepare_attend makes for `desc`: 1 or 2."""
+    n = load().kdt_tree_verify_prepare_attend_launches(ctypes.byref(desc))
+    if n < 0:
+        raise KdtError(load().kdt_last_status(), load().kdt_last_error().decode())
+    return n
 
 
 def _int32_2d(t, name):

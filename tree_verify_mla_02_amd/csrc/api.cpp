@@ -433,6 +433,59 @@ int kdt_tree_verify_combine(float *out, const kdt_verify_desc *desc, void *works
     return ok();
 }
 
+int kdt_tree_verify_prepare_attend(const int32_t *parents, uint64_t *bitmask, const int32_t *cache_lens,
+                                   const void *q_lat, const void *q_rope, const void *ckv_cache,
+                                   const void *krope_cache, const void *tree_ckv, const void *tree_krope, float scale,
+                                   float *out, const kdt_verify_desc *desc, void *workspace, size_t workspace_bytes,
+                                   int32_t *dev_status, void *stream) {
+    kdt::Geometry g;
+    int rc = geometry_for(desc, &g);
+    if (rc) return rc;
+    if (!kdt::fused_supported(*desc, g)) {
+        rc = kdt_tree_verify_prepare(parents, bitmask, cache_lens, desc, workspace, workspace_bytes, dev_status,
+                                     stream);
+        if (rc) return rc;
+        return kdt_tree_verify_attend(q_lat, q_rope, ckv_cache, krope_cache, tree_ckv, tree_krope, bitmask, scale,
+                                      out, desc, workspace, workspace_bytes, stream);
+    }
+    // the checks of kdt_tree_verify_prepare and kdt_tree_verify_attend
+    if (!parents || !bitmask || !cache_lens)
+        return fail(KDT_ERR_INVALID_ARG, "parents, bitmask and cache_lens must not be NULL");
+    if (((uintptr_t)parents & 3u) || ((uintptr_t)bitmask & 7u) || ((uintptr_t)cache_lens & 3u))
+        return fail(KDT_ERR_MISALIGNED, "parents and cache_lens must be 4-byte and bitmask 8-byte aligned");
+    const void *ptrs[] = {q_lat, q_rope, ckv_cache, krope_cache, tree_ckv, tree_krope, out};
+    const char *names[] = {"q_lat", "q_rope", "ckv_cache", "krope_cache", "tree_ckv", "tree_krope", "out"};
+    for (int k = 0; k < 7; k++) {
+        if (!ptrs[k] && !((k == 2 || k == 3) && desc->total_cache_len == 0))
+            return fail(KDT_ERR_INVALID_ARG, "%s is NULL", names[k]);
+        if (!aligned16(ptrs[k])) return fail(KDT_ERR_MISALIGNED, "%s is not 16-byte aligned", names[k]);
+    }
+    if (!std::isfinite(scale)) return fail(KDT_ERR_INVALID_ARG, "scale must be finite");
+    rc = check_ws(g, workspace, workspace_bytes);
+    if (rc) return rc;
+    kdt::AttnArgs a = make_args(*desc, g, workspace);
+    a.q_lat = q_lat;
+    a.q_rope = q_rope;
+    a.ckv = ckv_cache;
+    a.krope = krope_cache;
+    a.tckv = tree_ckv;
+    a.tkrope = tree_krope;
+    a.masks = bitmask;
+    a.out = out;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    const hipError_t e = kdt::launch_attend_fused(a, *desc, g, parents, bitmask, cache_lens, workspace, dev_status,
+                                                  (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prepare + attention launch");
+    return ok();
+}
+
+int kdt_tree_verify_prepare_attend_launches(const kdt_verify_desc *desc) {
+    kdt::Geometry g;
+    if (geometry_for(desc, &g)) return -1;
+    ok();
+    return kdt::fused_supported(*desc, g) ? 1 : 2;
+}
+
 int kdt_tree_verify_attn(const void *q_lat, const void *q_rope, const void *ckv_cache, const void *krope_cache,
                          const void *tree_ckv, const void *tree_krope, const uint64_t *bitmask,
                          const int32_t *cache_lens, float scale, float *out, const kdt_verify_desc *desc,

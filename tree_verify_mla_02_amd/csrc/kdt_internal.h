@@ -65,6 +65,27 @@ struct Unit {
 };
 static_assert(sizeof(Unit) == 32, "one 32-byte record");
 
+// Division by a divisor fixed for the launch (see fdiv in verify_attn.hip).
+struct FastDiv {
+    uint32_t d, m, l;
+};
+
+// What the one-launch path (masks, plan and attention of a one-request batch in the 64-row
+// kernel) needs beyond AttnArgs: the inputs of the masks and the plan, where the plan kernel
+// would have written its results, and the plan's group shape (see make_geometry).
+struct FusedPlan {
+    const int32_t *parents, *cache_lens;
+    uint64_t *masks_out;
+    int32_t *dev_status;
+    WsHeader *hdr;
+    int64_t *offsets;
+    int32_t *lens;
+    Unit *units;
+    int64_t max_len, total_len;
+    int RT, bt, bs, GR, GS, G, per;     // RT: row tiles of the unit list
+    FastDiv fd_chunk, fd_per, fd_bs, fd_gr;
+};
+
 struct AttnArgs {
     const void *q_lat, *q_rope, *ckv, *krope, *tckv, *tkrope;
     const uint64_t *masks;
@@ -84,6 +105,7 @@ struct AttnArgs {
     uint32_t *part_o;      // un-normalised partial outputs, per wave in register order: block
                            // ((b*S + s)*RT + rt)*4 + wave of 32 rows x d_c values, as packed
                            // 24-bit floats (bf16 inputs) or plain fp32 (fp32 inputs)
+    FusedPlan fp;          // one-launch path only
 };
 
 hipError_t launch_visibility(const int32_t *parents, int B, int N, uint64_t *masks,
@@ -96,6 +118,12 @@ hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t
 hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units,
                          hipStream_t st);
 hipError_t launch_combine(const AttnArgs &a, int d_latent, int dtype, hipStream_t st);
+// Masks, plan and attention of a one-request batch on 64-row workgroups in one launch; `a` as
+// for launch_attend.  fused_supported says whether desc and g allow it.
+bool fused_supported(const kdt_verify_desc &d, const Geometry &g);
+hipError_t launch_attend_fused(AttnArgs a, const kdt_verify_desc &d, const Geometry &g, const int32_t *parents,
+                               uint64_t *masks_out, const int32_t *cache_lens, void *ws, int32_t *dev_status,
+                               hipStream_t st);
 
 // 32-bit words of split-partial storage per 4 output values: 3 (24-bit floats) for bf16
 // inputs, 4 (fp32) for fp32 inputs.

@@ -78,9 +78,6 @@ constexpr int kMaxSortGroups = 2048;    // above this the groups keep request or
 // Multiplication", PLDI 1994): l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
 // t = mulhi(m, n), n / d = (t + ((n - t) >> 1)) >> (l - 1), and n / 1 = n.  The host sets the
 // constants; a hardware-less 32-bit division is a dependent chain of about forty instructions.
-struct FastDiv {
-    uint32_t d, m, l;
-};
 static inline FastDiv make_fastdiv(uint32_t d) {
     uint32_t l = 0;
     while (((uint64_t)1 << l) < d) l++;
@@ -1230,7 +1227,193 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *vbuf, int rot, const
     });
 }
 
-template <int DC, int DR>
+// ---- one-launch path of a one-request batch: plan unit and masks inside the attention
+// workgroups (the plan and visibility kernels' results, computed where they are used)
+
+// Work unit the plan kernel gives grid slot u when the batch is one request of L committed
+// keys (plan_body with B = 1).  The plan ranks its groups by work, longest first, ties by
+// index.  With one request a group's work depends only on its split block gs and never grows
+// with gs: block 0 holds split 0 and the tree keys, then come the blocks whose bs splits are
+// all full, then at most one partly filled block, then blocks past the last split.  So the
+// groups of equal work form runs of consecutive gs, and within a run the plan's order is the
+// index order (row block major).  Slot -> rank p follows the plan's snake dealing; rank p lies
+// in the run that contains gs = p / GR.
+// Branch-free, so that the kernel-argument loads it needs go out together at the start.
+__device__ __forceinline__ Unit fused_unit(const FusedPlan &f, int64_t chunk, int S, int L, uint32_t u) {
+    // splits_of without its 64-bit division: L + chunk - 1 < 2^32 (both below 2^31 + 64)
+    const uint32_t nsp = fdiv((uint32_t)(L > 0 ? L : 1) + (uint32_t)chunk - 1u, f.fd_chunk);
+    const int sb = nsp < (uint32_t)S ? (int)nsp : S;
+    const uint32_t x = u & (kXcds - 1), k = u >> 3;       // kXcds = 8
+    const uint32_t round = fdiv(k, f.fd_per);
+    const uint32_t i = k - round * (uint32_t)f.per;
+    const uint32_t p = round * kXcds + ((round & 1) ? kXcds - 1 - x : x);
+    const int E = (int)fdiv((uint32_t)(sb + f.bs - 1), f.fd_bs);     // blocks with a split
+    const int c = (int)fdiv(p, f.fd_gr);
+    // blocks 1 .. E-1 (E >= 2 when 0 < c < E): block E-1 holds L - (E-1)*span keys, at least 1
+    // and at most span, as many 64-key tiles as a full block when more than span - 64
+    const int64_t span = (int64_t)f.bs * chunk;           // a multiple of 64
+    const int fe = (L - (int64_t)(E - 1) * span > span - kKeysPerTile) ? E - 1 : E - 2;   // last full block
+    const bool mid = c > 0 && c < E, in_full = c <= fe;
+    const int lo = c == 0 ? 0 : mid ? (in_full ? 1 : E - 1) : E;
+    const int hi = c == 0 ? 0 : mid ? (in_full ? fe : E - 1) : f.GS - 1;
+    const uint32_t m = (uint32_t)(hi - lo + 1), q = p - (uint32_t)f.GR * (uint32_t)lo;
+    // q / m through a float reciprocal: q < G <= 2048, so the estimate is off by at most one
+    uint32_t gr = (uint32_t)((float)q * __builtin_amdgcn_rcpf((float)m));
+    gr = gr * m > q ? gr - 1 : gr;
+    gr = (gr + 1) * m <= q ? gr + 1 : gr;
+    const uint32_t gs = (uint32_t)lo + (q - gr * m);
+    const uint32_t ib = fdiv(i, f.fd_bs);
+    const int rt = (int)(gr * (uint32_t)f.bt + ib), sp = (int)(gs * (uint32_t)f.bs + (i - ib * (uint32_t)f.bs));
+    const int64_t k0 = (int64_t)sp * chunk;
+    const int64_t k1 = k0 + chunk < (int64_t)L ? k0 + chunk : (int64_t)L;
+    const bool valid = p < (uint32_t)f.G && rt < f.RT && sp < sb;
+    return valid ? Unit{0, rt, sp, sb, (int32_t)k0, (int32_t)k1, k0} : Unit{-1, 0, 0, 0, 0, 0, 0};
+}
+
+// One 4-byte-per-lane HBM -> LDS copy: lane l writes its dword at lds_addr + 4l (see lds_dma16).
+__device__ __forceinline__ void lds_dma4(const char *base, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 : : "v"(voff), "s"(base), "s"(lds_addr) : "m0");
+}
+
+// The masks of the request's N nodes in LDS (msk holds the final rows: zero for a node whose
+// path meets a bad parent link), built by fused_masks_wave while the workgroup's first tile
+// copies are in flight.
+struct FusedVis {
+    uint64_t msk[kMaxNodes][4];
+    int32_t jmp[kMaxNodes], bad[kMaxNodes];
+    int32_t par[kWaves][kMaxNodes];   // each wave's copy of parents[0 .. 255] (past N: the last)
+};
+
+// Copies parents[0 .. 64*ceil(N/64)) of request 0 into `par` (entries past N repeat the last),
+// one dword copy per 64 nodes, by the calling wave.  Completion is the caller's vmcnt wait.
+__device__ __forceinline__ void fused_parents_copy(int32_t *par, const int32_t *parents, int N, int lane) {
+    for (int j = 0; j < (N + 63) / 64; j++) {
+        const int idx = lane + 64 * j;
+        lds_dma4((const char *)parents, (uint32_t)(idx < N ? idx : N - 1) * 4u, (uint32_t)(uintptr_t)&par[64 * j]);
+    }
+}
+
+// All N masks from V.par[0] by wave 0 alone, which copied it (lane l holds nodes l + 64j, j < 4),
+// while the other waves go on.  The pointer jumping of visibility_rows, ceil(log2 N) rounds
+// through V, in which LDS serves this wave's reads and writes in program order: no barrier.  A
+// node keeps its own words in registers; V holds them for the nodes that jump to it.  Nodes
+// whose path meets a bad parent link get a zero row.  With masks_out, also writes the [N, W]
+// bitmask rows and raises KDT_DEV_BAD_PARENT as kdt_build_visibility does.
+__device__ __forceinline__ void fused_masks_wave(FusedVis &V, int N, int W, uint64_t *masks_out, int32_t *dev_status,
+                                                 int lane) {
+    constexpr int NS = kMaxNodes / 64;
+    wait_vm_all();
+    uint64_t w[NS][4];
+    int jmp[NS], bad[NS];
+#pragma unroll
+    for (int j = 0; j < NS; j++) {
+        const int i = lane + 64 * j;
+        jmp[j] = -1;
+        bad[j] = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) w[j][k] = k == j ? 1ull << lane : 0ull;
+        if (i < N) {
+            const int p = V.par[0][i];
+            bad[j] = p < -1 || p >= i;
+            jmp[j] = bad[j] ? -1 : p;
+#pragma unroll
+            for (int k = 0; k < 4; k++) V.msk[i][k] = w[j][k];
+            V.jmp[i] = jmp[j];
+            V.bad[i] = bad[j];
+        }
+    }
+    // after r rounds a node covers 2^r nodes of its path (or all of it); paths have <= N nodes
+    for (int n = 1; n < N; n <<= 1) {
+        uint64_t add[NS][4];
+        int nj[NS], nb[NS];
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            nj[j] = -1;
+            nb[j] = 0;
+#pragma unroll
+            for (int k = 0; k < 4; k++) add[j][k] = 0ull;
+            if (jmp[j] >= 0) {
+#pragma unroll
+                for (int k = 0; k < 4; k++) add[j][k] = V.msk[jmp[j]][k];
+                nj[j] = V.jmp[jmp[j]];
+                nb[j] = V.bad[jmp[j]];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            const int i = lane + 64 * j;
+            if (jmp[j] >= 0) {
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    w[j][k] |= add[j][k];
+                    V.msk[i][k] = w[j][k];
+                }
+                bad[j] |= nb[j];
+                jmp[j] = nj[j];
+                V.jmp[i] = jmp[j];
+                V.bad[i] = bad[j];
+            }
+        }
+    }
+    bool any_bad = false;
+#pragma unroll
+    for (int j = 0; j < NS; j++) {
+        const int i = lane + 64 * j;
+        if (i < N) {
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint64_t v = bad[j] ? 0ull : w[j][k];
+                V.msk[i][k] = v;
+                if (masks_out && k < W) masks_out[(int64_t)i * W + k] = v;
+            }
+            any_bad |= bad[j] != 0;
+        }
+    }
+    if (masks_out && dev_status && any_bad) atomicOr(dev_status, (int32_t)KDT_DEV_BAD_PARENT);
+}
+
+// Mask words of node n (< N) by a walk of its path, with the parents in VGPRs (lane l of
+// par_v[k] holds the parent of node l + 64k): the node index is wave-uniform, so each step is a
+// lane read and scalar work, no LDS access.  Zero when the path meets a parent link outside
+// [-1, j-1] (the rows visibility_rows rejects).
+__device__ __forceinline__ void node_mask_walk(const int (&par_v)[kMaxNodes / 64], int n, uint64_t (&m)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) m[k] = 0ull;
+    int j = n;
+    bool bad = false;
+    for (int step = 0; step <= n; step++) {       // a path has at most n + 1 nodes
+        const int hi = j >> 6, lo = j & 63;
+#pragma unroll
+        for (int k = 0; k < 4; k++) m[k] |= hi == k ? 1ull << lo : 0ull;
+        const int v = hi == 0 ? par_v[0] : hi == 1 ? par_v[1] : hi == 2 ? par_v[2] : par_v[3];
+        const int p = __builtin_amdgcn_readlane(v, lo);
+        if (p < -1 || p >= j) {
+            bad = true;
+            break;
+        }
+        if (p < 0) break;
+        j = p;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) m[k] = bad ? 0ull : m[k];
+}
+
+// The same for N <= 64: one mask word, the parents in one VGPR.
+__device__ __forceinline__ uint64_t node_mask_walk64(int par_v, int n) {
+    uint64_t m = 0ull;
+    int j = n;
+    for (int step = 0; step <= n; step++) {       // a path has at most n + 1 nodes
+        m |= 1ull << j;
+        const int p = __builtin_amdgcn_readlane(par_v, j);
+        if (p < -1 || p >= j) return 0ull;
+        if (p < 0) break;
+        j = p;
+    }
+    return m;
+}
+
+template <int DC, int DR, bool FUSED = false>
 __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     using T = __bf16;
     using Sh = Shape<T, DC, DR>;
@@ -1239,18 +1422,77 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     static_assert(Sh::BF16 && Sh::CB == 8, "bf16 rows of 8-chunk LDS blocks");
     __shared__ __attribute__((aligned(1024))) char smem[2 * Sh::TILE_BYTES];
     static_assert(2 * 64 * 256 * 4 + 2 * 64 * 8 <= 2 * Sh::TILE_BYTES, "merge buffers fit in the tile buffers");
+    __shared__ std::conditional_t<FUSED, FusedVis, char> fvis;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    const Unit unit = a.units[blockIdx.x];
-    if (unit.b < 0) return;
+    const int64_t R = a.R;
+    using Dma = TileDma<Sh, T>;
+    // The workgroup's first copies for unit u: tile 0 (its first cache tile, or the tree's
+    // first) into buffer 0 and the workgroup's rows (at most 64) into buffer 1, one round trip.
+    auto issue_first = [&](const Unit &u) {
+        const int64_t q0 = (int64_t)(a.tile_rows == 2 * kRowsPerWave ? u.rt : 0) * 2 * kRowsPerWave;
+        const int64_t nq = R - q0 < 2 * kRowsPerWave ? R - q0 : 2 * kRowsPerWave;
+        Dma d0, dq;
+        LDS_AS char *buf0 = (LDS_AS char *)smem, *buf1 = (LDS_AS char *)smem + Sh::TILE_BYTES;
+        if (u.k1 > u.k0) {
+            const int64_t left = (int64_t)u.k1 - u.k0;
+            d0.setup(buf0, (const T *)a.ckv, a.ckv_stride, (const T *)a.krope, a.krope_stride, u.row0,
+                     left < kKeysPerTile ? (int)left : kKeysPerTile, wave, lane);
+        } else {
+            d0.setup(buf0, (const T *)a.tckv, a.tckv_stride, (const T *)a.tkrope, a.tkrope_stride, (int64_t)u.b * a.N,
+                     a.N < kKeysPerTile ? a.N : kKeysPerTile, wave, lane);
+        }
+        d0.template issue<0, Dma::NINST>();
+        dq.setup(buf1, (const T *)a.q_lat, a.q_lat_stride, (const T *)a.q_rope, a.q_rope_stride, (int64_t)u.b * R + q0,
+                 (int)nq, wave, lane);
+        dq.template issue<0, Dma::NINST>();
+    };
+
+    Unit unit;
+    bool vis_full = false;          // builds all N masks (see below)
+    bool walk = false;              // takes tree keys: walks the paths of its own rows' nodes
+    bool writer = false;            // writes the masks and the plan's device status
+    if constexpr (FUSED) {
+        // the parents go out first (each wave its own copy): they arrive while the plan unit is
+        // worked out
+        fused_parents_copy(fvis.par[wave], a.fp.parents, a.N, lane);
+        // the plan, for this workgroup's slot only (one request: cache_lens[0] is all it reads)
+        const int L = a.fp.cache_lens[0];
+        const bool ok = L >= 0 && (int64_t)L <= a.fp.max_len && (int64_t)L <= a.fp.total_len;
+        unit = ok ? fused_unit(a.fp, a.chunk, a.S, L, blockIdx.x) : Unit{-1, 0, 0, 0, 0, 0, 0};
+        if (threadIdx.x == 0) {
+            a.fp.units[blockIdx.x] = unit;
+            if (blockIdx.x == 0) {
+                a.fp.hdr->ok = ok ? 1 : 0;
+                a.fp.lens[0] = L;
+                a.fp.offsets[0] = 0;
+                if (!ok && a.fp.dev_status) atomicOr(a.fp.dev_status, (int32_t)KDT_DEV_CACHE_LEN);
+            }
+        }
+        // One workgroup builds all N masks and writes them out: that of row tile 0 and the last
+        // split (without tree keys when there are several splits, so it has a tile to spare),
+        // or workgroup 0 of a rejected plan.  The others with tree keys need the masks of their
+        // own rows' nodes only, at most two per wave when H >= 32: a walk of each path.  With
+        // H < 32 they build all masks too.
+        writer = ok ? unit.rt == 0 && unit.s == unit.sb - 1 : blockIdx.x == 0;
+        vis_full = writer || (unit.b >= 0 && unit.s == 0 && a.H < kRowsPerWave);
+        walk = !vis_full && unit.b >= 0 && unit.s == 0;
+        if (unit.b < 0) {
+            if (vis_full && wave == 0) fused_masks_wave(fvis, a.N, a.W, a.fp.masks_out, a.fp.dev_status, lane);
+            wait_vm_all();          // no copy may still be landing when a workgroup exits
+            return;
+        }
+    } else {
+        unit = a.units[blockIdx.x];
+        if (unit.b < 0) return;
+    }
     const int b = unit.b, s = unit.s, sb = unit.sb;
     // 64-row tile of the unit: unit.rt counts 64-row tiles when the plan was made for them, and
     // is 0 for a request of at most 64 rows under 128-row tiles
     const int rt64 = a.tile_rows == 2 * kRowsPerWave ? unit.rt : 0;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rh = wave & 1, kh = wave >> 1;            // row half, key half
     const int half = lane >> 5;
-    const int64_t R = a.R;
     const int64_t row0 = (int64_t)rt64 * 2 * kRowsPerWave;          // the workgroup's first row
 
     const int64_t r = row0 + (int64_t)rh * kRowsPerWave + (lane & 31);
@@ -1264,7 +1506,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     const int n_tiles = n_cache + n_tree;
     const int64_t cache_row0 = unit.row0;
 
-    using Dma = TileDma<Sh, T>;
+    // copy setup of tile t into buffer bsel
     auto dma_setup = [&](Dma &d, int t, int bsel) {
         LDS_AS char *buf = (LDS_AS char *)smem + bsel * Sh::TILE_BYTES;
         if (t < n_cache) {
@@ -1280,19 +1522,42 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
                     lane);
         }
     };
-    {
-        Dma d0;
-        dma_setup(d0, 0, 0);
-        d0.template issue<0, Dma::NINST>();
-    }
-    // the workgroup's rows (at most 64) go to buffer 1 together with tile 0: one round trip
     LDS_AS char *qbuf = (LDS_AS char *)smem + Sh::TILE_BYTES;
-    {
-        const int64_t nrows = R - row0 < 2 * kRowsPerWave ? R - row0 : 2 * kRowsPerWave;
-        Dma dq;
-        dq.setup(qbuf, (const T *)a.q_lat, a.q_lat_stride, (const T *)a.q_rope, a.q_rope_stride,
-                 (int64_t)b * R + row0, (int)nrows, wave, lane);
-        dq.template issue<0, Dma::NINST>();
+    issue_first(unit);
+    if constexpr (FUSED) {
+        if (vis_full) {
+            // while the copies land
+            if (wave == 0)
+                fused_masks_wave(fvis, a.N, a.W, writer ? a.fp.masks_out : nullptr, writer ? a.fp.dev_status : nullptr,
+                                 lane);
+        } else if (walk) {
+            // the masks of this wave's rows' nodes (at most two), into fvis for the tree tiles,
+            // while the copies land.  This wave's parents copy went out before its last 2*NINST
+            // copies (loads complete in order).  The two waves of a row half write the same words.
+            asm volatile("s_waitcnt vmcnt(%0)" : : "i"(2 * Dma::NINST) : "memory");
+            // the rows' nodes as the tile loop takes them: rows past R read row R - 1
+            const int64_t r_first = row0 + (int64_t)rh * kRowsPerWave, r_last = r_first + kRowsPerWave - 1;
+            const int64_t r_lo = r_first < R ? r_first : R - 1, r_hi = r_last < R ? r_last : R - 1;
+            const int n_lo = (int)(r_lo / a.H), n_hi = (int)(r_hi / a.H);
+            if (a.N <= 64) {
+                const int par_v = fvis.par[wave][lane];
+                const uint64_t m_lo = node_mask_walk64(par_v, n_lo);
+                const uint64_t m_hi = n_hi != n_lo ? node_mask_walk64(par_v, n_hi) : m_lo;
+                if (lane < 4) fvis.msk[n_lo][lane] = lane == 0 ? m_lo : 0ull;
+                if (n_hi != n_lo && lane < 4) fvis.msk[n_hi][lane] = lane == 0 ? m_hi : 0ull;
+            } else {
+                int par_v[kMaxNodes / 64];
+#pragma unroll
+                for (int k = 0; k < kMaxNodes / 64; k++) par_v[k] = fvis.par[wave][lane + 64 * k];
+                uint64_t m[4];
+                node_mask_walk(par_v, n_lo, m);
+                if (lane < 4) fvis.msk[n_lo][lane] = lane == 0 ? m[0] : lane == 1 ? m[1] : lane == 2 ? m[2] : m[3];
+                if (n_hi != n_lo) {
+                    node_mask_walk(par_v, n_hi, m);
+                    if (lane < 4) fvis.msk[n_hi][lane] = lane == 0 ? m[0] : lane == 1 ? m[1] : lane == 2 ? m[2] : m[3];
+                }
+            }
+        }
     }
 
     constexpr int QK_PAT = Sh::CB / 2;
@@ -1348,7 +1613,11 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
         } else {
             const int tt = t - n_cache;
             const int nvalid = a.N - tt * kKeysPerTile;
-            uint64_t vis = a.masks[((int64_t)b * a.N + node) * a.W + tt];
+            uint64_t vis;
+            if constexpr (FUSED)
+                vis = fvis.msk[node][tt];
+            else
+                vis = a.masks[((int64_t)b * a.N + node) * a.W + tt];
             if (nvalid < kKeysPerTile) vis &= (1ull << nvalid) - 1ull;
             wv = block_bits(vis, kh, half);
             need_mask = true;
@@ -1653,6 +1922,45 @@ hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype,
         verify_attn_kernel<float, 64, 16><<<grid, block, 0, st>>>(a);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+bool fused_supported(const kdt_verify_desc &d, const Geometry &g) {
+    // one request on 64-row tiles, groups the plan sorts (<= kMaxSortGroups) and work keys
+    // that do not saturate (fewer than 0xfffff tiles per group)
+    return d.batch == 1 && g.tile_rows == 2 * kRowsPerWave && d.dtype == KDT_BF16 && d.d_latent == 512 &&
+           d.d_rope == 64 && g.groups <= kMaxSortGroups && g.units <= INT32_MAX &&
+           d.max_cache_len + d.num_nodes < (int64_t)0xfffff * kKeysPerTile;
+}
+
+hipError_t launch_attend_fused(AttnArgs a, const kdt_verify_desc &d, const Geometry &g, const int32_t *parents,
+                               uint64_t *masks_out, const int32_t *cache_lens, void *ws, int32_t *dev_status,
+                               hipStream_t st) {
+    if (!fused_supported(d, g)) return hipErrorInvalidValue;
+    char *w = (char *)ws;
+    FusedPlan &f = a.fp;
+    f.parents = parents;
+    f.cache_lens = cache_lens;
+    f.masks_out = masks_out;
+    f.dev_status = dev_status;
+    f.hdr = (WsHeader *)(w + g.off_header);
+    f.offsets = (int64_t *)(w + g.off_offsets);
+    f.lens = (int32_t *)(w + g.off_lens);
+    f.units = (Unit *)(w + g.off_units);
+    f.max_len = d.max_cache_len;
+    f.total_len = d.total_cache_len;
+    f.RT = g.row_tiles;
+    f.bt = g.bt;
+    f.bs = g.bs;
+    f.GR = (g.row_tiles + g.bt - 1) / g.bt;
+    f.GS = (g.nsplit + g.bs - 1) / g.bs;
+    f.G = (int)g.groups;
+    f.per = g.bt * g.bs;
+    f.fd_chunk = make_fastdiv((uint32_t)g.chunk);
+    f.fd_per = make_fastdiv((uint32_t)f.per);
+    f.fd_bs = make_fastdiv((uint32_t)f.bs);
+    f.fd_gr = make_fastdiv((uint32_t)f.GR);
+    decode_attn_kernel<512, 64, true><<<dim3((unsigned)g.units), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 
