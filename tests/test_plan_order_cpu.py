@@ -15,15 +15,16 @@ import random
 import pytest
 
 
-def _geometry(rows, max_len, cus=256, tile_rows=64, min_chunk=256):
-    """The host geometry of a one-request batch on 64-row tiles (make_geometry)."""
+def _geometry(rows, max_len, cus=256, tile_rows=64, min_chunk=256, bs_many=2):
+    """The host geometry of a one-request batch on 64-row tiles (make_geometry; bs_many = 4 is
+    the 128-row tiles' split block, also checked so that the closed form is not tied to one)."""
     rt = -(-rows // tile_rows)
     S = 1
     if rt < 2 * cus and max_len > min_chunk:
         S = max(1, min(-(-cus // rt), -(-max_len // min_chunk)))
     chunk = max(64, -(-(-(-max_len // S) if max_len > 0 else 64) // 64) * 64)
     S = max(1, -(-max_len // chunk)) if max_len > 0 else 1
-    bs = 4 if (S >= 4 and rt >= 16) else 1
+    bs = bs_many if (S >= 4 and rt >= 16) else 1
     bt = -(-rt // 4) if bs > 1 else rt
     groups = lambda: (-(-rt // bt)) * (-(-S // bs))
     while groups() < 8 and bt > 1:
@@ -122,12 +123,13 @@ def _cases():
 def test_closed_form_equals_plan_order():
     n = 0
     for rows, N, max_len, L in _cases():
-        RT, S, chunk, bt, bs, U = _geometry(rows, max_len)
-        a = plan_units(L, N, RT, S, chunk, bt, bs, U, max_len)
-        b = closed_form_units(L, N, RT, S, chunk, bt, bs, U, max_len)
-        assert a == b, (rows, N, max_len, L)
-        n += 1
-    assert n > 2000
+        for bs_many in (2, 4):
+            RT, S, chunk, bt, bs, U = _geometry(rows, max_len, bs_many=bs_many)
+            a = plan_units(L, N, RT, S, chunk, bt, bs, U, max_len)
+            b = closed_form_units(L, N, RT, S, chunk, bt, bs, U, max_len)
+            assert a == b, (rows, N, max_len, L, bs_many)
+            n += 1
+    assert n > 4000
 
 
 @pytest.mark.parametrize("wrong", ["ties_by_split", "no_partial_run"])

@@ -196,8 +196,11 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     // A request with many row tiles and splits (the Kimi shape: 32 x 8) would then have every
     // XCD fetch all of its queries at once when the kernel starts; blocks of RT/4 row tiles x
     // 4 splits cut that burst to a quarter for twice the key traffic, which measured faster
-    // (56.8 vs 60.5 us there; 16 x 2 blocks: 57.7 us).
-    x.bs = (S >= 4 && rt >= 16) ? 4 : 1;
+    // (56.8 vs 60.5 us there; 16 x 2 blocks: 57.7 us).  On 64-row tiles (the Kimi shape there
+    // is 64 x 4) a query tile is half as large, and blocks of 16 row tiles x 2 splits read a
+    // third less from beyond L2 than 8 x 4 (29.0 against 43.5 MB per launch) in the same time;
+    // 32 x 1 reads as little but measured 1.6 us slower (the query burst again).
+    x.bs = (S >= 4 && rt >= 16) ? (x.tile_rows == kRowsPerTile ? 4 : 2) : 1;
     x.bt = (int)(x.bs > 1 ? (rt + 3) / 4 : rt);
     // A group runs on one XCD, so fewer groups than XCDs would leave XCDs idle (one request
     // of 128 row tiles with 2 splits would run on 2 of the 8): halve the row-tile blocks until
