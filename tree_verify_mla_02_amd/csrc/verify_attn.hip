@@ -1077,6 +1077,10 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             }
 #pragma unroll
             for (int kb = 0; kb < 2; kb++) {
+                // A block that no row of the wave sees (past the last key of a partial tile, or
+                // tree keys off every row's path) would add nothing: all its scores are -inf, so
+                // P = 0 and the reference stays.  The half-0 lanes' words hold all 32 of its keys.
+                if (need_mask && __ballot((kb ? w1 : w0) != 0u) == 0) continue;
                 f32x16 sc = (f32x16){};
 #pragma unroll
                 for (int kk = 0; kk < NQ; kk++) {
