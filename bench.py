@@ -5,9 +5,10 @@
 
 A step is one pass of the whole path over one synthetic batch already resident in HBM:
 ancestor bitmasks from the parent array, the ragged plan, the attention and the split combine.
-For one request on 64-row tiles (the Kimi shape, decode, small trees) the masks and the plan
-are made inside the attention launch (kdt_tree_verify_prepare_attend): two launches per step;
-other shapes, and --staged, run masks + plan as a launch of their own.  The default workload is
+For one request of bf16 inputs (the Kimi shape, decode, small trees, chains and prefill chunks)
+the masks and the plan are made inside the attention launch (kdt_tree_verify_prepare_attend):
+two launches per step; several requests, fp32 inputs, and --staged, run masks + plan as a launch
+of their own.  The default workload is
 the Kimi/DeepSeekV3-shape request (H = 64 heads, latent 512 + rope 64, bf16, committed cache
 4096 tokens, a 64-node best-first draft tree).
 
@@ -136,8 +137,8 @@ def run(args):
     out = torch.empty((sp.batch, sp.nodes, sp.heads, dc), dtype=torch.float32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    # masks, plan and attention in one launch where the shape allows (one request on 64-row
-    # tiles), else prepare and attend; --staged times the three launches everywhere
+    # masks, plan and attention in one launch where the batch allows (one bf16 request), else
+    # prepare and attend; --staged times the three launches everywhere
     one_launch = not getattr(args, "staged", False) and kdt.prepare_attend_launches(desc) == 1
 
     def prep():

@@ -183,11 +183,13 @@ int kdt_tree_verify_prepare(const int32_t *parents, uint64_t *bitmask, const int
  * out or the split partials hold the attention; kdt_tree_verify_combine follows as after
  * kdt_tree_verify_attend), in one launch where the shape allows.  A verify step needs the
  * visibility masks ("Validating the Native Engine", section "The Broader Context") and the ragged
- * plan before its attention.  For a one-request batch on 64-row workgroups (a decode step, small
- * trees, the Kimi-size tree over short caches; kdt_tree_verify_prepare_attend_launches() == 1)
- * both are made inside the attention launch: each workgroup works out the unit the plan would
- * give its grid slot from cache_lens[0]; workgroups with tree keys walk the root paths of their
- * rows' nodes; one workgroup builds all masks for bitmask.  Other shapes run the two stages.
+ * plan before its attention.  For a one-request batch of bf16 512 + 64 inputs
+ * (kdt_tree_verify_prepare_attend_launches() == 1) both are made inside the attention launch:
+ * each workgroup works out the unit the plan would give its grid slot from cache_lens[0]; on
+ * 64-row workgroups (a decode step, small trees, trees of up to 8192 rows over short caches) the
+ * workgroups with tree keys walk the root paths of their rows' nodes, on 128-row ones (longer
+ * caches, prefill chains) they build all masks by pointer jumping; one workgroup writes bitmask.
+ * Other batches run the two stages.
  * Results are bit-identical to the staged calls (the workspace included); a caller that reuses
  * one plan for every layer still uses the staged calls.
  */

@@ -1,9 +1,9 @@
 """kdt_tree_verify_prepare_attend against the staged calls (prepare, then attend) it replaces,
 each followed by combine.
 
-For a one-request batch on 64-row workgroups the call works out the plan unit of every grid
-slot and the visibility masks inside the attention launch (one launch); every other shape runs
-the two stages.  Either way its results must be the staged results bit for bit: the masks, the
+For a one-request batch of bf16 512 + 64 inputs, on 64- or 128-row workgroups, the call works
+out the plan unit of every grid slot and the visibility masks inside the attention launch (one
+launch); every other batch runs the two stages.  Either way its results must be the staged results bit for bit: the masks, the
 outputs, the whole workspace (plan header, offsets, lengths, unit list, split partials) and the
 device status.  Both workspaces start zeroed, so bytes nobody writes compare equal too.  The
 staged path itself is held to the oracle by the parity tests; one one-launch case is also
@@ -38,6 +38,14 @@ CASES = {
     "h48": (S("fh48", 86, 1, 10, 48, 512, 64, "bf16", 3000, tree="random"), 1),
     # 16 heads (< 32): every workgroup with tree keys builds all masks; a 32-node chain
     "h16chain": (S("fh16", 87, 1, 32, 16, 512, 64, "bf16", 2000, tree="chain"), 1),
+    # 128-row workgroups: the 16-node chain over 32768 keys (32 splits)
+    "chain": ("chain", 3),
+    # a 256-node causal chunk over 4096 keys: 128 row tiles, 2 splits, four mask words
+    "prefill4k": ("prefill4k", 3),
+    # 256 random-tree nodes x 4 heads over 20000 keys: 8 row tiles, 256-node masks
+    "t128n256": (S("ft128", 88, 1, 256, 4, 512, 64, "bf16", 20000, tree="random"), 1),
+    # 1000 rows (last row tile partly filled) over 9000 keys, 8 heads
+    "t128rows1000": (S("ft1000", 89, 1, 125, 8, 512, 64, "bf16", 9000, tree="random"), 1),
 }
 
 
@@ -104,27 +112,30 @@ def test_fused_against_oracle_kimi():
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("L", [0, 1, 63, 64, 65, 1000, 1024, 1025, 4095])
-def test_fused_shorter_cache(L):
+@pytest.mark.parametrize("base,L", [("kimi", L) for L in (0, 1, 63, 64, 65, 1000, 1024, 1025, 4095)] +
+                         [("chain", L) for L in (0, 1, 1023, 1025, 20000, 32767)])
+def test_fused_shorter_cache(base, L):
     """cache_lens[0] below the bound the geometry was made for: fewer splits, partial splits."""
-    inp = _inputs("kimi")
+    inp = _inputs(base)
     dev = to_device(inp)
+    maxL = int(inp.cache_lens.max())
     lens = torch.tensor([L], dtype=torch.int32, device="cuda")
-    staged = _run(inp, dev, lens, fused=False, max_len=4096)
-    fused = _run(inp, dev, lens, fused=True, max_len=4096)
-    _same(fused, staged, f"L={L}")
+    staged = _run(inp, dev, lens, fused=False, max_len=maxL)
+    fused = _run(inp, dev, lens, fused=True, max_len=maxL)
+    _same(fused, staged, f"{base} L={L}")
 
 
-@pytest.mark.parametrize("L", [4097, -1])
-def test_fused_rejected_cache_len(L):
+@pytest.mark.parametrize("base,L", [("kimi", 4097), ("kimi", -1), ("chain", 32769), ("chain", -1)])
+def test_fused_rejected_cache_len(base, L):
     """A length outside [0, max_cache_len]: KDT_DEV_CACHE_LEN, outputs untouched, masks still
     written -- as the staged calls do."""
-    inp = _inputs("kimi")
+    inp = _inputs(base)
     dev = to_device(inp)
+    maxL = int(inp.cache_lens.max())
     lens = torch.tensor([L], dtype=torch.int32, device="cuda")
-    staged = _run(inp, dev, lens, fused=False, max_len=4096)
-    fused = _run(inp, dev, lens, fused=True, max_len=4096)
-    _same(fused, staged, f"L={L}")
+    staged = _run(inp, dev, lens, fused=False, max_len=maxL)
+    fused = _run(inp, dev, lens, fused=True, max_len=maxL)
+    _same(fused, staged, f"{base} L={L}")
     assert fused[3] == 2                         # KDT_DEV_CACHE_LEN
     assert torch.isnan(fused[1]).all()
 
@@ -139,13 +150,14 @@ def test_fused_total_len_bound():
     assert fused[3] == 2
 
 
-def test_fused_bad_parent():
+@pytest.mark.parametrize("base", ["kimi", "chain"])
+def test_fused_bad_parent(base):
     """A parent link outside [-1, j-1]: the rows whose path meets it get zero masks and
     KDT_DEV_BAD_PARENT, as the staged masks do."""
-    inp = _inputs("kimi")
+    inp = _inputs(base)
     parents = inp.parents.clone()
-    parents[0, 9] = 40                          # not below 9
-    parents[0, 30] = -7
+    parents[0, 9] = 12                          # not below 9
+    parents[0, 14 if base == "chain" else 30] = -7
     inp = workloads.Inputs(inp.spec, parents, inp.cache_lens, inp.q_lat, inp.q_rope, inp.kv_cache, inp.tree_kv,
                            inp.scale)
     dev = to_device(inp)
@@ -153,15 +165,17 @@ def test_fused_bad_parent():
     fused = _run(inp, dev, dev.cache_lens, fused=True)
     _same(fused, staged, "bad parent")
     assert fused[3] == 1                         # KDT_DEV_BAD_PARENT
-    assert (fused[0][0, 9] == 0).all() and (fused[0][0, 30] == 0).all()
+    assert (fused[0][0, 9] == 0).all() and (fused[0][0, 14 if base == "chain" else 30] == 0).all()
+    if base == "chain":                         # every later node of the chain passes through 9
+        assert (fused[0][0, 9:] == 0).all()
 
 
-@pytest.mark.parametrize("name", ["t64_ragged", "chain_short", "tiny"])
+@pytest.mark.parametrize("name", ["t64_ragged", "two_chains", "tiny"])
 def test_fused_other_shapes_run_the_stages(name):
-    """Shapes the one-launch path does not take (several requests, 128-row tiles, fp32) give
-    the staged results through the same call (two launches)."""
+    """Batches the one-launch path does not take (several requests on either tile size, fp32)
+    give the staged results through the same call (two launches)."""
     spec = {"t64_ragged": S("t64r", 72, 3, 40, 64, 512, 64, "bf16", None, ragged=(0, 3000)),
-            "chain_short": S("chs", 85, 1, 16, 64, 512, 64, "bf16", 32768, tree="chain"),
+            "two_chains": S("chs2", 85, 2, 16, 64, 512, 64, "bf16", 20000, tree="chain"),
             "tiny": "tiny"}[name]
     inp = workloads.make_inputs(spec, seed=4)
     dev = to_device(inp)
@@ -171,9 +185,10 @@ def test_fused_other_shapes_run_the_stages(name):
     _same(fused, staged, name)
 
 
-def test_fused_in_graph():
+@pytest.mark.parametrize("base", ["kimi", "chain"])
+def test_fused_in_graph(base):
     """prepare_attend + combine captured in a graph and replayed, with eager work between replays."""
-    inp = _inputs("kimi")
+    inp = _inputs(base)
     dev = to_device(inp)
     eager = _run(inp, dev, dev.cache_lens, fused=True)
     desc = eager[4]

@@ -15,9 +15,10 @@ import random
 import pytest
 
 
-def _geometry(rows, max_len, cus=256, tile_rows=64, min_chunk=256, bs_many=2):
-    """The host geometry of a one-request batch on 64-row tiles (make_geometry; bs_many = 4 is
-    the 128-row tiles' split block, also checked so that the closed form is not tied to one)."""
+def _geometry(rows, max_len, cus=256, tile_rows=64, min_chunk=256):
+    """The host geometry of a one-request batch (make_geometry): split blocks of 2 on 64-row
+    tiles, 4 on 128-row tiles."""
+    bs_many = 2 if tile_rows == 64 else 4
     rt = -(-rows // tile_rows)
     S = 1
     if rt < 2 * cus and max_len > min_chunk:
@@ -108,11 +109,12 @@ def closed_form_units(L, N, RT, S, chunk, bt, bs, U, max_len):
 
 def _cases():
     rng = random.Random(7)
-    shapes = [(4096, 64, 4096), (64, 1, 32768), (448, 7, 4096), (2560, 40, 2999), (8192, 128, 8192), (480, 10, 3000)]
+    shapes = [(4096, 64, 4096), (64, 1, 32768), (448, 7, 4096), (2560, 40, 2999), (8192, 128, 8192), (480, 10, 3000),
+              (1024, 16, 32768), (16384, 256, 4096), (16384, 256, 32768), (1000, 125, 5000)]
     while len(shapes) < 400:
         N = rng.randint(1, 256)
         rows = N * rng.choice([1, 2, 8, 16, 48, 64, 128])
-        if rows <= 8192:
+        if rows <= 16384:
             shapes.append((rows, N, rng.choice([0, 1, 64, 65, 256, 257, 1000, 4096, 8192, rng.randint(0, 40000)])))
     for rows, N, max_len in shapes:
         for L in sorted({0, 1, max_len, max(0, max_len - 1), max_len // 2, max_len + 1, -1,
@@ -123,11 +125,11 @@ def _cases():
 def test_closed_form_equals_plan_order():
     n = 0
     for rows, N, max_len, L in _cases():
-        for bs_many in (2, 4):
-            RT, S, chunk, bt, bs, U = _geometry(rows, max_len, bs_many=bs_many)
+        for tile_rows in (64, 128):
+            RT, S, chunk, bt, bs, U = _geometry(rows, max_len, tile_rows=tile_rows)
             a = plan_units(L, N, RT, S, chunk, bt, bs, U, max_len)
             b = closed_form_units(L, N, RT, S, chunk, bt, bs, U, max_len)
-            assert a == b, (rows, N, max_len, L, bs_many)
+            assert a == b, (rows, N, max_len, L, tile_rows)
             n += 1
     assert n > 4000
 

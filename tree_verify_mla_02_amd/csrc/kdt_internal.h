@@ -70,8 +70,8 @@ struct FastDiv {
     uint32_t d, m, l;
 };
 
-// What the one-launch path (masks, plan and attention of a one-request batch in the 64-row
-// kernel) needs beyond AttnArgs: the inputs of the masks and the plan, where the plan kernel
+// What the one-launch path (masks, plan and attention of a one-request batch in one attention
+// launch) needs beyond AttnArgs: the inputs of the masks and the plan, where the plan kernel
 // would have written its results, and the plan's group shape (see make_geometry).
 struct FusedPlan {
     const int32_t *parents, *cache_lens;
@@ -118,8 +118,8 @@ hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t
 hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units,
                          hipStream_t st);
 hipError_t launch_combine(const AttnArgs &a, int d_latent, int dtype, hipStream_t st);
-// Masks, plan and attention of a one-request batch on 64-row workgroups in one launch; `a` as
-// for launch_attend.  fused_supported says whether desc and g allow it.
+// Masks, plan and attention of a one-request batch in one launch (64- or 128-row workgroups, as
+// the geometry says); `a` as for launch_attend.  fused_supported says whether desc and g allow it.
 bool fused_supported(const kdt_verify_desc &d, const Geometry &g);
 hipError_t launch_attend_fused(AttnArgs a, const kdt_verify_desc &d, const Geometry &g, const int32_t *parents,
                                uint64_t *masks_out, const int32_t *cache_lens, void *ws, int32_t *dev_status,

@@ -847,21 +847,238 @@ __device__ __forceinline__ float4 load_part4(const uint32_t *src) {
         return unpack24x4(src);
 }
 
-template <typename T, int DC, int DR>
+// ---- one-launch path of a one-request batch: plan unit and masks inside the attention
+// workgroups (the plan and visibility kernels' results, computed where they are used)
+
+// Work unit the plan kernel gives grid slot u when the batch is one request of L committed
+// keys (plan_body with B = 1).  The plan ranks its groups by work, longest first, ties by
+// index.  With one request a group's work depends only on its split block gs and never grows
+// with gs: block 0 holds split 0 and the tree keys, then come the blocks whose bs splits are
+// all full, then at most one partly filled block, then blocks past the last split.  So the
+// groups of equal work form runs of consecutive gs, and within a run the plan's order is the
+// index order (row block major).  Slot -> rank p follows the plan's snake dealing; rank p lies
+// in the run that contains gs = p / GR.
+// Branch-free, so that the kernel-argument loads it needs go out together at the start.
+__device__ __forceinline__ Unit fused_unit(const FusedPlan &f, int64_t chunk, int S, int L, uint32_t u) {
+    // splits_of without its 64-bit division: L + chunk - 1 < 2^32 (both below 2^31 + 64)
+    const uint32_t nsp = fdiv((uint32_t)(L > 0 ? L : 1) + (uint32_t)chunk - 1u, f.fd_chunk);
+    const int sb = nsp < (uint32_t)S ? (int)nsp : S;
+    const uint32_t x = u & (kXcds - 1), k = u >> 3;       // kXcds = 8
+    const uint32_t round = fdiv(k, f.fd_per);
+    const uint32_t i = k - round * (uint32_t)f.per;
+    const uint32_t p = round * kXcds + ((round & 1) ? kXcds - 1 - x : x);
+    const int E = (int)fdiv((uint32_t)(sb + f.bs - 1), f.fd_bs);     // blocks with a split
+    const int c = (int)fdiv(p, f.fd_gr);
+    // blocks 1 .. E-1 (E >= 2 when 0 < c < E): block E-1 holds L - (E-1)*span keys, at least 1
+    // and at most span, as many 64-key tiles as a full block when more than span - 64
+    const int64_t span = (int64_t)f.bs * chunk;           // a multiple of 64
+    const int fe = (L - (int64_t)(E - 1) * span > span - kKeysPerTile) ? E - 1 : E - 2;   // last full block
+    const bool mid = c > 0 && c < E, in_full = c <= fe;
+    const int lo = c == 0 ? 0 : mid ? (in_full ? 1 : E - 1) : E;
+    const int hi = c == 0 ? 0 : mid ? (in_full ? fe : E - 1) : f.GS - 1;
+    const uint32_t m = (uint32_t)(hi - lo + 1), q = p - (uint32_t)f.GR * (uint32_t)lo;
+    // q / m through a float reciprocal: q < G <= 2048, so the estimate is off by at most one
+    uint32_t gr = (uint32_t)((float)q * __builtin_amdgcn_rcpf((float)m));
+    gr = gr * m > q ? gr - 1 : gr;
+    gr = (gr + 1) * m <= q ? gr + 1 : gr;
+    const uint32_t gs = (uint32_t)lo + (q - gr * m);
+    const uint32_t ib = fdiv(i, f.fd_bs);
+    const int rt = (int)(gr * (uint32_t)f.bt + ib), sp = (int)(gs * (uint32_t)f.bs + (i - ib * (uint32_t)f.bs));
+    const int64_t k0 = (int64_t)sp * chunk;
+    const int64_t k1 = k0 + chunk < (int64_t)L ? k0 + chunk : (int64_t)L;
+    const bool valid = p < (uint32_t)f.G && rt < f.RT && sp < sb;
+    return valid ? Unit{0, rt, sp, sb, (int32_t)k0, (int32_t)k1, k0} : Unit{-1, 0, 0, 0, 0, 0, 0};
+}
+
+// One 4-byte-per-lane HBM -> LDS copy: lane l writes its dword at lds_addr + 4l (see lds_dma16).
+__device__ __forceinline__ void lds_dma4(const char *base, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+                 : : "v"(voff), "s"(base), "s"(lds_addr) : "m0");
+}
+
+// The masks of the request's N nodes in LDS (msk[k][n] holds word k of node n's final row: zero
+// for a node whose path meets a bad parent link), built by fused_masks_wave while the
+// workgroup's first copies are in flight.  Word-major, so that the lanes of a wave, which hold
+// consecutive nodes, touch consecutive 8-byte words (node-major rows 32 bytes apart put every
+// eight lanes on the same banks).
+struct FusedVis {
+    uint64_t msk[4][kMaxNodes];
+    int32_t jmp[kMaxNodes], bad[kMaxNodes];
+    int32_t par[kWaves][kMaxNodes];   // each wave's copy of parents[0 .. 255] (past N: the last)
+};
+
+// Copies parents[0 .. 64*ceil(N/64)) of request 0 into `par` (entries past N repeat the last),
+// one dword copy per 64 nodes, by the calling wave.  Completion is the caller's vmcnt wait.
+__device__ __forceinline__ void fused_parents_copy(int32_t *par, const int32_t *parents, int N, int lane) {
+    for (int j = 0; j < (N + 63) / 64; j++) {
+        const int idx = lane + 64 * j;
+        lds_dma4((const char *)parents, (uint32_t)(idx < N ? idx : N - 1) * 4u, (uint32_t)(uintptr_t)&par[64 * j]);
+    }
+}
+
+// All N masks from V.par[0] by wave 0 alone, which copied it (lane l holds nodes l + 64j, j < 4),
+// while the other waves go on; the caller has waited for that copy.  The pointer jumping of visibility_rows, ceil(log2 N) rounds
+// through V, in which LDS serves this wave's reads and writes in program order: no barrier.  A
+// node keeps its own words in registers; V holds them for the nodes that jump to it.  Nodes
+// whose path meets a bad parent link get a zero row.  With masks_out, also writes the [N, W]
+// bitmask rows and raises KDT_DEV_BAD_PARENT as kdt_build_visibility does.
+__device__ __forceinline__ void fused_masks_wave(FusedVis &V, int N, int W, uint64_t *masks_out, int32_t *dev_status,
+                                                 int lane) {
+    constexpr int NS = kMaxNodes / 64;
+    uint64_t w[NS][4];
+    int jmp[NS], bad[NS];
+#pragma unroll
+    for (int j = 0; j < NS; j++) {
+        const int i = lane + 64 * j;
+        jmp[j] = -1;
+        bad[j] = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) w[j][k] = k == j ? 1ull << lane : 0ull;
+        if (i < N) {
+            const int p = V.par[0][i];
+            bad[j] = p < -1 || p >= i;
+            jmp[j] = bad[j] ? -1 : p;
+#pragma unroll
+            for (int k = 0; k < 4; k++) V.msk[k][i] = w[j][k];
+            V.jmp[i] = jmp[j];
+            V.bad[i] = bad[j];
+        }
+    }
+    // after r rounds a node covers 2^r nodes of its path (or all of it); paths have <= N nodes
+    for (int n = 1; n < N; n <<= 1) {
+        uint64_t add[NS][4];
+        int nj[NS], nb[NS];
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            nj[j] = -1;
+            nb[j] = 0;
+#pragma unroll
+            for (int k = 0; k < 4; k++) add[j][k] = 0ull;
+            if (jmp[j] >= 0) {
+#pragma unroll
+                for (int k = 0; k < 4; k++) add[j][k] = V.msk[k][jmp[j]];
+                nj[j] = V.jmp[jmp[j]];
+                nb[j] = V.bad[jmp[j]];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            const int i = lane + 64 * j;
+            if (jmp[j] >= 0) {
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    w[j][k] |= add[j][k];
+                    V.msk[k][i] = w[j][k];
+                }
+                bad[j] |= nb[j];
+                jmp[j] = nj[j];
+                V.jmp[i] = jmp[j];
+                V.bad[i] = bad[j];
+            }
+        }
+    }
+    bool any_bad = false;
+#pragma unroll
+    for (int j = 0; j < NS; j++) {
+        const int i = lane + 64 * j;
+        if (i < N) {
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint64_t v = bad[j] ? 0ull : w[j][k];
+                V.msk[k][i] = v;
+                if (masks_out && k < W) masks_out[(int64_t)i * W + k] = v;
+            }
+            any_bad |= bad[j] != 0;
+        }
+    }
+    if (masks_out && dev_status && any_bad) atomicOr(dev_status, (int32_t)KDT_DEV_BAD_PARENT);
+}
+
+// Mask words of node n (< N) by a walk of its path, with the parents in VGPRs (lane l of
+// par_v[k] holds the parent of node l + 64k): the node index is wave-uniform, so each step is a
+// lane read and scalar work, no LDS access.  Zero when the path meets a parent link outside
+// [-1, j-1] (the rows visibility_rows rejects).
+__device__ __forceinline__ void node_mask_walk(const int (&par_v)[kMaxNodes / 64], int n, uint64_t (&m)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) m[k] = 0ull;
+    int j = n;
+    bool bad = false;
+    for (int step = 0; step <= n; step++) {       // a path has at most n + 1 nodes
+        const int hi = j >> 6, lo = j & 63;
+#pragma unroll
+        for (int k = 0; k < 4; k++) m[k] |= hi == k ? 1ull << lo : 0ull;
+        const int v = hi == 0 ? par_v[0] : hi == 1 ? par_v[1] : hi == 2 ? par_v[2] : par_v[3];
+        const int p = __builtin_amdgcn_readlane(v, lo);
+        if (p < -1 || p >= j) {
+            bad = true;
+            break;
+        }
+        if (p < 0) break;
+        j = p;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; k++) m[k] = bad ? 0ull : m[k];
+}
+
+// The same for N <= 64: one mask word, the parents in one VGPR.
+__device__ __forceinline__ uint64_t node_mask_walk64(int par_v, int n) {
+    uint64_t m = 0ull;
+    int j = n;
+    for (int step = 0; step <= n; step++) {       // a path has at most n + 1 nodes
+        m |= 1ull << j;
+        const int p = __builtin_amdgcn_readlane(par_v, j);
+        if (p < -1 || p >= j) return 0ull;
+        if (p < 0) break;
+        j = p;
+    }
+    return m;
+}
+
+template <typename T, int DC, int DR, bool FUSED = false>
 __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
     using Sh = Shape<T, DC, DR>;
     constexpr int D = Sh::D;
     constexpr int NT16 = DC / 32;                       // 32-wide output column tiles
     constexpr int NQ = Sh::BF16 ? D / 16 : D / 2;       // query fragments per lane
     __shared__ __attribute__((aligned(1024))) char smem[2 * Sh::TILE_BYTES];
-
-    // One scalar load: a slot the plan left empty (or every slot, when it rejected the
-    // cache lengths) has b < 0.
-    const Unit unit = a.units[blockIdx.x];
-    if (unit.b < 0) return;
-    const int b = unit.b, rt = unit.rt, s = unit.s, sb = unit.sb;
+    __shared__ std::conditional_t<FUSED, FusedVis, char> fvis;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: keeps LDS bases in SGPRs
+
+    Unit unit;
+    bool vis_full = false;          // builds all N masks: every workgroup with tree keys, and the writer
+    bool writer = false;            // writes the masks and the plan's device status
+    if constexpr (FUSED) {
+        // One request: this slot's plan unit from cache_lens[0], as in the 64-row kernel.  Chains
+        // (a prefill chunk) make root paths as long as the tree, so the workgroups with tree keys
+        // build all masks by pointer jumping (log2 N rounds) rather than walking their nodes' paths.
+        fused_parents_copy(fvis.par[wave], a.fp.parents, a.N, lane);
+        const int L = a.fp.cache_lens[0];
+        const bool ok = L >= 0 && (int64_t)L <= a.fp.max_len && (int64_t)L <= a.fp.total_len;
+        unit = ok ? fused_unit(a.fp, a.chunk, a.S, L, blockIdx.x) : Unit{-1, 0, 0, 0, 0, 0, 0};
+        if (threadIdx.x == 0) {
+            a.fp.units[blockIdx.x] = unit;
+            if (blockIdx.x == 0) {
+                a.fp.hdr->ok = ok ? 1 : 0;
+                a.fp.lens[0] = L;
+                a.fp.offsets[0] = 0;
+                if (!ok && a.fp.dev_status) atomicOr(a.fp.dev_status, (int32_t)KDT_DEV_CACHE_LEN);
+            }
+        }
+        writer = ok ? unit.rt == 0 && unit.s == unit.sb - 1 : blockIdx.x == 0;
+        vis_full = writer || (unit.b >= 0 && unit.s == 0);
+        if (unit.b < 0) {
+            wait_vm_all();          // the parents copy; no copy may still be landing when a workgroup exits
+            if (vis_full && wave == 0) fused_masks_wave(fvis, a.N, a.W, a.fp.masks_out, a.fp.dev_status, lane);
+            return;
+        }
+    } else {
+        // One scalar load: a slot the plan left empty (or every slot, when it rejected the
+        // cache lengths) has b < 0.
+        unit = a.units[blockIdx.x];
+        if (unit.b < 0) return;
+    }
+    const int b = unit.b, rt = unit.rt, s = unit.s, sb = unit.sb;
     const int half = lane >> 5;                          // 0: lanes 0-31, 1: lanes 32-63
     const int64_t R = a.R;
 
@@ -940,6 +1157,15 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
                      (int64_t)b * R + first, nrows < 64 ? (int)nrows : 64, wave, lane);
             if (h == 1) __syncthreads();       // waves 0 and 1 are done reading half 0
             dq.template issue<0, Dma::NINST>();
+            if constexpr (FUSED) {
+                if (h == 0 && vis_full && wave == 0) {
+                    // the masks while tile 0 and the first query rows land: the parents copy
+                    // went out before their 2 * NINST copies (loads complete in order)
+                    asm volatile("s_waitcnt vmcnt(%0)" : : "i"(2 * Dma::NINST) : "memory");
+                    fused_masks_wave(fvis, a.N, a.W, writer ? a.fp.masks_out : nullptr,
+                                     writer ? a.fp.dev_status : nullptr, lane);
+                }
+            }
             wait_vm_all();
             __syncthreads();
             if (wave / 2 == h) {
@@ -995,7 +1221,11 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
         } else {
             const int tt = t - n_cache;
             const int nvalid = a.N - tt * kKeysPerTile;
-            uint64_t vis = a.masks[((int64_t)b * a.N + node) * a.W + tt];
+            uint64_t vis;
+            if constexpr (FUSED)
+                vis = fvis.msk[tt][node];
+            else
+                vis = a.masks[((int64_t)b * a.N + node) * a.W + tt];
             if (nvalid < kKeysPerTile) vis &= (1ull << nvalid) - 1ull;
             w0 = block_bits(vis, 0, half);
             w1 = block_bits(vis, 1, half);
@@ -1231,192 +1461,6 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *vbuf, int rot, const
     });
 }
 
-// ---- one-launch path of a one-request batch: plan unit and masks inside the attention
-// workgroups (the plan and visibility kernels' results, computed where they are used)
-
-// Work unit the plan kernel gives grid slot u when the batch is one request of L committed
-// keys (plan_body with B = 1).  The plan ranks its groups by work, longest first, ties by
-// index.  With one request a group's work depends only on its split block gs and never grows
-// with gs: block 0 holds split 0 and the tree keys, then come the blocks whose bs splits are
-// all full, then at most one partly filled block, then blocks past the last split.  So the
-// groups of equal work form runs of consecutive gs, and within a run the plan's order is the
-// index order (row block major).  Slot -> rank p follows the plan's snake dealing; rank p lies
-// in the run that contains gs = p / GR.
-// Branch-free, so that the kernel-argument loads it needs go out together at the start.
-__device__ __forceinline__ Unit fused_unit(const FusedPlan &f, int64_t chunk, int S, int L, uint32_t u) {
-    // splits_of without its 64-bit division: L + chunk - 1 < 2^32 (both below 2^31 + 64)
-    const uint32_t nsp = fdiv((uint32_t)(L > 0 ? L : 1) + (uint32_t)chunk - 1u, f.fd_chunk);
-    const int sb = nsp < (uint32_t)S ? (int)nsp : S;
-    const uint32_t x = u & (kXcds - 1), k = u >> 3;       // kXcds = 8
-    const uint32_t round = fdiv(k, f.fd_per);
-    const uint32_t i = k - round * (uint32_t)f.per;
-    const uint32_t p = round * kXcds + ((round & 1) ? kXcds - 1 - x : x);
-    const int E = (int)fdiv((uint32_t)(sb + f.bs - 1), f.fd_bs);     // blocks with a split
-    const int c = (int)fdiv(p, f.fd_gr);
-    // blocks 1 .. E-1 (E >= 2 when 0 < c < E): block E-1 holds L - (E-1)*span keys, at least 1
-    // and at most span, as many 64-key tiles as a full block when more than span - 64
-    const int64_t span = (int64_t)f.bs * chunk;           // a multiple of 64
-    const int fe = (L - (int64_t)(E - 1) * span > span - kKeysPerTile) ? E - 1 : E - 2;   // last full block
-    const bool mid = c > 0 && c < E, in_full = c <= fe;
-    const int lo = c == 0 ? 0 : mid ? (in_full ? 1 : E - 1) : E;
-    const int hi = c == 0 ? 0 : mid ? (in_full ? fe : E - 1) : f.GS - 1;
-    const uint32_t m = (uint32_t)(hi - lo + 1), q = p - (uint32_t)f.GR * (uint32_t)lo;
-    // q / m through a float reciprocal: q < G <= 2048, so the estimate is off by at most one
-    uint32_t gr = (uint32_t)((float)q * __builtin_amdgcn_rcpf((float)m));
-    gr = gr * m > q ? gr - 1 : gr;
-    gr = (gr + 1) * m <= q ? gr + 1 : gr;
-    const uint32_t gs = (uint32_t)lo + (q - gr * m);
-    const uint32_t ib = fdiv(i, f.fd_bs);
-    const int rt = (int)(gr * (uint32_t)f.bt + ib), sp = (int)(gs * (uint32_t)f.bs + (i - ib * (uint32_t)f.bs));
-    const int64_t k0 = (int64_t)sp * chunk;
-    const int64_t k1 = k0 + chunk < (int64_t)L ? k0 + chunk : (int64_t)L;
-    const bool valid = p < (uint32_t)f.G && rt < f.RT && sp < sb;
-    return valid ? Unit{0, rt, sp, sb, (int32_t)k0, (int32_t)k1, k0} : Unit{-1, 0, 0, 0, 0, 0, 0};
-}
-
-// One 4-byte-per-lane HBM -> LDS copy: lane l writes its dword at lds_addr + 4l (see lds_dma16).
-__device__ __forceinline__ void lds_dma4(const char *base, uint32_t voff, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-                 : : "v"(voff), "s"(base), "s"(lds_addr) : "m0");
-}
-
-// The masks of the request's N nodes in LDS (msk holds the final rows: zero for a node whose
-// path meets a bad parent link), built by fused_masks_wave while the workgroup's first tile
-// copies are in flight.
-struct FusedVis {
-    uint64_t msk[kMaxNodes][4];
-    int32_t jmp[kMaxNodes], bad[kMaxNodes];
-    int32_t par[kWaves][kMaxNodes];   // each wave's copy of parents[0 .. 255] (past N: the last)
-};
-
-// Copies parents[0 .. 64*ceil(N/64)) of request 0 into `par` (entries past N repeat the last),
-// one dword copy per 64 nodes, by the calling wave.  Completion is the caller's vmcnt wait.
-__device__ __forceinline__ void fused_parents_copy(int32_t *par, const int32_t *parents, int N, int lane) {
-    for (int j = 0; j < (N + 63) / 64; j++) {
-        const int idx = lane + 64 * j;
-        lds_dma4((const char *)parents, (uint32_t)(idx < N ? idx : N - 1) * 4u, (uint32_t)(uintptr_t)&par[64 * j]);
-    }
-}
-
-// All N masks from V.par[0] by wave 0 alone, which copied it (lane l holds nodes l + 64j, j < 4),
-// while the other waves go on.  The pointer jumping of visibility_rows, ceil(log2 N) rounds
-// through V, in which LDS serves this wave's reads and writes in program order: no barrier.  A
-// node keeps its own words in registers; V holds them for the nodes that jump to it.  Nodes
-// whose path meets a bad parent link get a zero row.  With masks_out, also writes the [N, W]
-// bitmask rows and raises KDT_DEV_BAD_PARENT as kdt_build_visibility does.
-__device__ __forceinline__ void fused_masks_wave(FusedVis &V, int N, int W, uint64_t *masks_out, int32_t *dev_status,
-                                                 int lane) {
-    constexpr int NS = kMaxNodes / 64;
-    wait_vm_all();
-    uint64_t w[NS][4];
-    int jmp[NS], bad[NS];
-#pragma unroll
-    for (int j = 0; j < NS; j++) {
-        const int i = lane + 64 * j;
-        jmp[j] = -1;
-        bad[j] = 0;
-#pragma unroll
-        for (int k = 0; k < 4; k++) w[j][k] = k == j ? 1ull << lane : 0ull;
-        if (i < N) {
-            const int p = V.par[0][i];
-            bad[j] = p < -1 || p >= i;
-            jmp[j] = bad[j] ? -1 : p;
-#pragma unroll
-            for (int k = 0; k < 4; k++) V.msk[i][k] = w[j][k];
-            V.jmp[i] = jmp[j];
-            V.bad[i] = bad[j];
-        }
-    }
-    // after r rounds a node covers 2^r nodes of its path (or all of it); paths have <= N nodes
-    for (int n = 1; n < N; n <<= 1) {
-        uint64_t add[NS][4];
-        int nj[NS], nb[NS];
-#pragma unroll
-        for (int j = 0; j < NS; j++) {
-            nj[j] = -1;
-            nb[j] = 0;
-#pragma unroll
-            for (int k = 0; k < 4; k++) add[j][k] = 0ull;
-            if (jmp[j] >= 0) {
-#pragma unroll
-                for (int k = 0; k < 4; k++) add[j][k] = V.msk[jmp[j]][k];
-                nj[j] = V.jmp[jmp[j]];
-                nb[j] = V.bad[jmp[j]];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NS; j++) {
-            const int i = lane + 64 * j;
-            if (jmp[j] >= 0) {
-#pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    w[j][k] |= add[j][k];
-                    V.msk[i][k] = w[j][k];
-                }
-                bad[j] |= nb[j];
-                jmp[j] = nj[j];
-                V.jmp[i] = jmp[j];
-                V.bad[i] = bad[j];
-            }
-        }
-    }
-    bool any_bad = false;
-#pragma unroll
-    for (int j = 0; j < NS; j++) {
-        const int i = lane + 64 * j;
-        if (i < N) {
-#pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint64_t v = bad[j] ? 0ull : w[j][k];
-                V.msk[i][k] = v;
-                if (masks_out && k < W) masks_out[(int64_t)i * W + k] = v;
-            }
-            any_bad |= bad[j] != 0;
-        }
-    }
-    if (masks_out && dev_status && any_bad) atomicOr(dev_status, (int32_t)KDT_DEV_BAD_PARENT);
-}
-
-// Mask words of node n (< N) by a walk of its path, with the parents in VGPRs (lane l of
-// par_v[k] holds the parent of node l + 64k): the node index is wave-uniform, so each step is a
-// lane read and scalar work, no LDS access.  Zero when the path meets a parent link outside
-// [-1, j-1] (the rows visibility_rows rejects).
-__device__ __forceinline__ void node_mask_walk(const int (&par_v)[kMaxNodes / 64], int n, uint64_t (&m)[4]) {
-#pragma unroll
-    for (int k = 0; k < 4; k++) m[k] = 0ull;
-    int j = n;
-    bool bad = false;
-    for (int step = 0; step <= n; step++) {       // a path has at most n + 1 nodes
-        const int hi = j >> 6, lo = j & 63;
-#pragma unroll
-        for (int k = 0; k < 4; k++) m[k] |= hi == k ? 1ull << lo : 0ull;
-        const int v = hi == 0 ? par_v[0] : hi == 1 ? par_v[1] : hi == 2 ? par_v[2] : par_v[3];
-        const int p = __builtin_amdgcn_readlane(v, lo);
-        if (p < -1 || p >= j) {
-            bad = true;
-            break;
-        }
-        if (p < 0) break;
-        j = p;
-    }
-#pragma unroll
-    for (int k = 0; k < 4; k++) m[k] = bad ? 0ull : m[k];
-}
-
-// The same for N <= 64: one mask word, the parents in one VGPR.
-__device__ __forceinline__ uint64_t node_mask_walk64(int par_v, int n) {
-    uint64_t m = 0ull;
-    int j = n;
-    for (int step = 0; step <= n; step++) {       // a path has at most n + 1 nodes
-        m |= 1ull << j;
-        const int p = __builtin_amdgcn_readlane(par_v, j);
-        if (p < -1 || p >= j) return 0ull;
-        if (p < 0) break;
-        j = p;
-    }
-    return m;
-}
-
 template <int DC, int DR, bool FUSED = false>
 __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     using T = __bf16;
@@ -1483,8 +1527,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
         vis_full = writer || (unit.b >= 0 && unit.s == 0 && a.H < kRowsPerWave);
         walk = !vis_full && unit.b >= 0 && unit.s == 0;
         if (unit.b < 0) {
+            wait_vm_all();          // the parents copy; no copy may still be landing when a workgroup exits
             if (vis_full && wave == 0) fused_masks_wave(fvis, a.N, a.W, a.fp.masks_out, a.fp.dev_status, lane);
-            wait_vm_all();          // no copy may still be landing when a workgroup exits
             return;
         }
     } else {
@@ -1531,9 +1575,11 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     if constexpr (FUSED) {
         if (vis_full) {
             // while the copies land
-            if (wave == 0)
+            if (wave == 0) {
+                wait_vm_all();
                 fused_masks_wave(fvis, a.N, a.W, writer ? a.fp.masks_out : nullptr, writer ? a.fp.dev_status : nullptr,
                                  lane);
+            }
         } else if (walk) {
             // the masks of this wave's rows' nodes (at most two), into fvis for the tree tiles,
             // while the copies land.  This wave's parents copy went out before its last 2*NINST
@@ -1547,18 +1593,18 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
                 const int par_v = fvis.par[wave][lane];
                 const uint64_t m_lo = node_mask_walk64(par_v, n_lo);
                 const uint64_t m_hi = n_hi != n_lo ? node_mask_walk64(par_v, n_hi) : m_lo;
-                if (lane < 4) fvis.msk[n_lo][lane] = lane == 0 ? m_lo : 0ull;
-                if (n_hi != n_lo && lane < 4) fvis.msk[n_hi][lane] = lane == 0 ? m_hi : 0ull;
+                if (lane < 4) fvis.msk[lane][n_lo] = lane == 0 ? m_lo : 0ull;
+                if (n_hi != n_lo && lane < 4) fvis.msk[lane][n_hi] = lane == 0 ? m_hi : 0ull;
             } else {
                 int par_v[kMaxNodes / 64];
 #pragma unroll
                 for (int k = 0; k < kMaxNodes / 64; k++) par_v[k] = fvis.par[wave][lane + 64 * k];
                 uint64_t m[4];
                 node_mask_walk(par_v, n_lo, m);
-                if (lane < 4) fvis.msk[n_lo][lane] = lane == 0 ? m[0] : lane == 1 ? m[1] : lane == 2 ? m[2] : m[3];
+                if (lane < 4) fvis.msk[lane][n_lo] = lane == 0 ? m[0] : lane == 1 ? m[1] : lane == 2 ? m[2] : m[3];
                 if (n_hi != n_lo) {
                     node_mask_walk(par_v, n_hi, m);
-                    if (lane < 4) fvis.msk[n_hi][lane] = lane == 0 ? m[0] : lane == 1 ? m[1] : lane == 2 ? m[2] : m[3];
+                    if (lane < 4) fvis.msk[lane][n_hi] = lane == 0 ? m[0] : lane == 1 ? m[1] : lane == 2 ? m[2] : m[3];
                 }
             }
         }
@@ -1619,7 +1665,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
             const int nvalid = a.N - tt * kKeysPerTile;
             uint64_t vis;
             if constexpr (FUSED)
-                vis = fvis.msk[node][tt];
+                vis = fvis.msk[tt][node];
             else
                 vis = a.masks[((int64_t)b * a.N + node) * a.W + tt];
             if (nvalid < kKeysPerTile) vis &= (1ull << nvalid) - 1ull;
@@ -1930,10 +1976,10 @@ hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype,
 }
 
 bool fused_supported(const kdt_verify_desc &d, const Geometry &g) {
-    // one request on 64-row tiles, groups the plan sorts (<= kMaxSortGroups) and work keys
-    // that do not saturate (fewer than 0xfffff tiles per group)
-    return d.batch == 1 && g.tile_rows == 2 * kRowsPerWave && d.dtype == KDT_BF16 && d.d_latent == 512 &&
-           d.d_rope == 64 && g.groups <= kMaxSortGroups && g.units <= INT32_MAX &&
+    // one bf16 512 + 64 request (either tile size), groups the plan sorts (<= kMaxSortGroups)
+    // and work keys that do not saturate (fewer than 0xfffff tiles per group)
+    return d.batch == 1 && d.dtype == KDT_BF16 && d.d_latent == 512 && d.d_rope == 64 &&
+           g.groups <= kMaxSortGroups && g.units <= INT32_MAX &&
            d.max_cache_len + d.num_nodes < (int64_t)0xfffff * kKeysPerTile;
 }
 
@@ -1964,7 +2010,10 @@ hipError_t launch_attend_fused(AttnArgs a, const kdt_verify_desc &d, const Geome
     f.fd_per = make_fastdiv((uint32_t)f.per);
     f.fd_bs = make_fastdiv((uint32_t)f.bs);
     f.fd_gr = make_fastdiv((uint32_t)f.GR);
-    decode_attn_kernel<512, 64, true><<<dim3((unsigned)g.units), dim3(256), 0, st>>>(a);
+    if (g.tile_rows == 2 * kRowsPerWave)
+        decode_attn_kernel<512, 64, true><<<dim3((unsigned)g.units), dim3(256), 0, st>>>(a);
+    else
+        verify_attn_kernel<__bf16, 512, 64, true><<<dim3((unsigned)g.units), dim3(256), 0, st>>>(a);
     return hipGetLastError();
 }
 
