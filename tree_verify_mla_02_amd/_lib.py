@@ -231,7 +231,7 @@ def combine(out, desc: VerifyDesc, workspace, stream=None):
 def prepare_attend(parents, cache_lens, q_lat, q_rope, ckv, krope, tree_ckv, tree_krope, scale, out,
                    desc: VerifyDesc, workspace, masks_out: Optional[torch.Tensor] = None, dev_status=None,
                    stream=None) -> torch.Tensor:
-    """prepare + attend in one call (one launch for one request on 64-row tiles); combine
+    """prepare + attend in one call (one launch for a one-request bf16 batch); combine
     follows as after attend.  Returns the masks [B, N, ceil(N/64)] (int64 view of uint64)."""
     if parents.dtype != torch.int32 or not parents.is_contiguous() or parents.dim() != 2:
         raise ValueError("parents must be a contiguous [B, N] int32 tensor")

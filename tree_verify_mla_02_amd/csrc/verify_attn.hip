@@ -28,6 +28,10 @@
 //     masked with the row's 64-bit ancestor word.
 //   * Small batches split the committed keys over workgroups; partial (O, max, sum) are
 //     merged by a log-sum-exp combine.
+//   * Requests that 128-row workgroups cannot spread over the GPU take 64-row ones
+//     (decode_attn_kernel: waves split the rows and the keys of each tile).
+//   * For a one-request batch both kernels can also make the visibility masks and the plan
+//     unit inside the attention launch (their FUSED instantiations), saving a launch.
 #include "kdt_internal.h"
 #include "visibility_rows.h"
 
