@@ -54,11 +54,21 @@ def run_gpu(inp: workloads.Inputs, dev: DevInputs = None, staged=False):
 
     staged: False = kdt_build_visibility + kdt_tree_verify_attn; True = visibility, plan,
     attend, combine as separate calls; "prepare" = kdt_tree_verify_prepare (masks and plan
-    in one launch), attend, combine."""
+    in one launch), attend, combine; "one" = kdt_tree_verify_prepare_attend (masks, plan and
+    attention in one launch where the batch allows), combine."""
     dev = dev or to_device(inp)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     maxL = int(inp.cache_lens.max()) if inp.cache_lens.numel() else 0
     total = inp.total_len
+    if staged == "one":
+        desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, maxL, total)
+        ws = kdt.alloc_workspace(desc)
+        out = torch.empty(dev.q_lat.shape, dtype=torch.float32, device="cuda")
+        masks = kdt.prepare_attend(dev.parents, dev.cache_lens, dev.q_lat, dev.q_rope, dev.ckv, dev.krope,
+                                   dev.tree_ckv, dev.tree_krope, inp.scale, out, desc, ws, dev_status=status)
+        kdt.combine(out, desc, ws)
+        torch.cuda.synchronize()
+        return masks.cpu().numpy().view(np.uint64), out, int(status.item())
     if staged == "prepare":
         desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, maxL, total)
         ws = kdt.alloc_workspace(desc)

@@ -1,8 +1,9 @@
 """GPU edge cases of the attention kernels, through the C ABI, against closed forms and the fp64
 oracle.  Each property is run on every attention kernel the library builds:
 
-  k128   bf16, d = 512 + 64, 1024 rows per request: the 128-row kernel, keys split
+  k128   bf16, d = 512 + 64, 1024 rows over 9000 keys: the 128-row kernel, keys split
   k64    bf16, d = 512 + 64, 128 rows per request: the 64-row kernel, keys split
+  k64w   bf16, d = 512 + 64, 1024 rows over 1500 keys: the 64-row kernel, 16 row tiles
   bf16s  bf16, d = 64 + 16: the 128-row kernel at small dims
   f32    fp32, d = 64 + 16: the fp32 instantiation (fp32 split partials)
 
@@ -23,6 +24,8 @@ every drafted continuation is verified in one pass as if decoded alone):
 Also: batches past the plan's LDS capacity (more than 1024 requests, more than 2048 groups), fp32
 requests with outputs of magnitude 1-4 over long caches (split partials in fp32), and causal
 prefill of chains of 256 nodes and of longer sequences in 256-node chunks.
+The bf16 512 + 64 cases, all one-request batches, also run through the one-launch call
+(kdt_tree_verify_prepare_attend), whose outputs must equal the staged calls' bit for bit.
 """
 import dataclasses
 
@@ -38,11 +41,22 @@ from gpu_helpers import TOL, report, run_gpu, to_device
 pytestmark = pytest.mark.gpu
 
 KERNELS = {
-    "k128": workloads.Spec("e128", 70, 1, 16, 64, 512, 64, "bf16", 1500, tree="random"),
+    # over 8192 keys: 128-row tiles (shorter caches take 64-row ones up to 8192 rows)
+    "k128": workloads.Spec("e128", 70, 1, 16, 64, 512, 64, "bf16", 9000, tree="random"),
     "k64": workloads.Spec("e64", 71, 1, 2, 64, 512, 64, "bf16", 1300, tree="chain"),
+    "k64w": workloads.Spec("e64w", 75, 1, 16, 64, 512, 64, "bf16", 1500, tree="random"),
     "bf16s": workloads.Spec("es", 72, 2, 9, 8, 64, 16, "bf16", 700, tree="random"),
     "f32": workloads.Spec("ef", 73, 2, 8, 4, 64, 16, "f32", 700, tree="random"),
 }
+
+
+def test_k128_takes_128_row_tiles():
+    """k128 must run the 128-row kernel: for 1024 rows over 9000 keys 128-row tiles make 29 splits
+    of 320 keys (64-row tiles would make 16)."""
+    inp = workloads.make_inputs(KERNELS["k128"], seed=0)
+    dev = to_device(inp)
+    desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, 9000, inp.total_len)
+    assert kdt.num_splits(desc) == 29
 
 
 def _cast(x: np.ndarray, like: torch.Tensor) -> torch.Tensor:
@@ -66,7 +80,9 @@ def _paths(parents: np.ndarray):
 
 
 def _gpu_vs_oracle(name, inp, tol=None):
-    """Every row of the GPU output against the oracle; returns (gpu out, oracle out) as fp64."""
+    """Every row of the GPU output against the oracle; returns (gpu out, oracle out) as fp64.
+    A one-request bf16 512 + 64 batch also runs through the one-launch call, which must give the
+    staged calls' bits."""
     _, out, status = run_gpu(inp)
     assert status == 0
     got = out.cpu().double().numpy()
@@ -76,6 +92,14 @@ def _gpu_vs_oracle(name, inp, tol=None):
     tol = TOL[inp.spec.dtype] if tol is None else tol
     report(name, err, tol)
     assert err <= tol
+    sp = inp.spec
+    if sp.batch == 1 and sp.dtype == "bf16" and sp.d_latent == 512:
+        dev = to_device(inp)
+        _, staged, _ = run_gpu(inp, dev, staged="prepare")
+        _, one, st1 = run_gpu(inp, dev, staged="one")
+        assert st1 == 0
+        assert torch.equal(one.view(torch.int32), staged.view(torch.int32)), f"{name}: one launch differs"
+        print(f"PASS {name}: one launch bit-identical to the staged calls", flush=True)
     return got, ref
 
 
@@ -207,7 +231,7 @@ def test_head_permutation_is_exact(kern):
     print(f"PASS head permutation bit-identical [{kern}]", flush=True)
 
 
-@pytest.mark.parametrize("kern", ["k128", "k64", "f32"])
+@pytest.mark.parametrize("kern", ["k128", "k64", "k64w", "f32"])
 def test_node_relabel_permutes_outputs(kern):
     """Another parents-first numbering of the same tree (children of a node in reverse order,
     found by a depth-first walk) permutes the outputs."""
