@@ -38,6 +38,9 @@ CASES = {
     "h48": (S("fh48", 86, 1, 10, 48, 512, 64, "bf16", 3000, tree="random"), 1),
     # 16 heads (< 32): every workgroup with tree keys builds all masks; a 32-node chain
     "h16chain": (S("fh16", 87, 1, 32, 16, 512, 64, "bf16", 2000, tree="chain"), 1),
+    # deep paths on 64-row tiles: a 64-node chain (masks in registers) and a 128-node one (in LDS)
+    "chain64": (S("fc64", 90, 1, 64, 64, 512, 64, "bf16", 4096, tree="chain"), 1),
+    "chain128": (S("fc128", 91, 1, 128, 64, 512, 64, "bf16", 8192, tree="chain"), 1),
     # 128-row workgroups: the 16-node chain over 32768 keys (32 splits)
     "chain": ("chain", 3),
     # a 256-node causal chunk over 4096 keys: 128 row tiles, 2 splits, four mask words

@@ -998,44 +998,30 @@ __device__ __forceinline__ void fused_masks_wave(FusedVis &V, int N, int W, uint
     if (masks_out && dev_status && any_bad) atomicOr(dev_status, (int32_t)KDT_DEV_BAD_PARENT);
 }
 
-// Mask words of node n (< N) by a walk of its path, with the parents in VGPRs (lane l of
-// par_v[k] holds the parent of node l + 64k): the node index is wave-uniform, so each step is a
-// lane read and scalar work, no LDS access.  Zero when the path meets a parent link outside
-// [-1, j-1] (the rows visibility_rows rejects).
-__device__ __forceinline__ void node_mask_walk(const int (&par_v)[kMaxNodes / 64], int n, uint64_t (&m)[4]) {
-#pragma unroll
-    for (int k = 0; k < 4; k++) m[k] = 0ull;
-    int j = n;
-    bool bad = false;
-    for (int step = 0; step <= n; step++) {       // a path has at most n + 1 nodes
-        const int hi = j >> 6, lo = j & 63;
-#pragma unroll
-        for (int k = 0; k < 4; k++) m[k] |= hi == k ? 1ull << lo : 0ull;
-        const int v = hi == 0 ? par_v[0] : hi == 1 ? par_v[1] : hi == 2 ? par_v[2] : par_v[3];
-        const int p = __builtin_amdgcn_readlane(v, lo);
-        if (p < -1 || p >= j) {
-            bad = true;
-            break;
+// All masks of a tree of N <= 64 nodes by pointer jumping in registers, every lane at once: lane
+// l holds node l's parent and its own mask word; each round a lane ORs in the word of the node it
+// jumps to and takes over that node's jump and bad flag, read with ds_bpermute (a cross-lane
+// read through the LDS crossbar, no LDS memory).  ceil(log2 N) rounds cover any path, however
+// deep.  Returns lane l's word (zero when its path meets a parent link outside [-1, j-1], the rows
+// visibility_rows rejects; zero for lanes >= N).
+__device__ __forceinline__ uint64_t masks64_jump(int par, int N, int lane) {
+    const bool in = lane < N;
+    int bad = in && (par < -1 || par >= lane);
+    int jmp = in && !bad ? par : -1;
+    uint64_t m = in ? 1ull << lane : 0ull;
+    for (int n = 1; n < N; n <<= 1) {
+        const int addr = (jmp >= 0 ? jmp : lane) * 4;
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)m);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(uint32_t)(m >> 32));
+        const int nj = __builtin_amdgcn_ds_bpermute(addr, jmp);
+        const int nb = __builtin_amdgcn_ds_bpermute(addr, bad);
+        if (jmp >= 0) {
+            m |= ((uint64_t)hi << 32) | lo;
+            bad |= nb;
+            jmp = nj;
         }
-        if (p < 0) break;
-        j = p;
     }
-#pragma unroll
-    for (int k = 0; k < 4; k++) m[k] = bad ? 0ull : m[k];
-}
-
-// The same for N <= 64: one mask word, the parents in one VGPR.
-__device__ __forceinline__ uint64_t node_mask_walk64(int par_v, int n) {
-    uint64_t m = 0ull;
-    int j = n;
-    for (int step = 0; step <= n; step++) {       // a path has at most n + 1 nodes
-        m |= 1ull << j;
-        const int p = __builtin_amdgcn_readlane(par_v, j);
-        if (p < -1 || p >= j) return 0ull;
-        if (p < 0) break;
-        j = p;
-    }
-    return m;
+    return bad ? 0ull : m;
 }
 
 template <typename T, int DC, int DR, bool FUSED = false>
@@ -1503,7 +1489,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
 
     Unit unit;
     bool vis_full = false;          // builds all N masks (see below)
-    bool walk = false;              // takes tree keys: walks the paths of its own rows' nodes
+    bool own = false;               // takes tree keys: works out the masks in registers (N <= 64)
     bool writer = false;            // writes the masks and the plan's device status
     if constexpr (FUSED) {
         // the parents go out first (each wave its own copy): they arrive while the plan unit is
@@ -1524,12 +1510,14 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
         }
         // One workgroup builds all N masks and writes them out: that of row tile 0 and the last
         // split (without tree keys when there are several splits, so it has a tile to spare),
-        // or workgroup 0 of a rejected plan.  The others with tree keys need the masks of their
-        // own rows' nodes only, at most two per wave when H >= 32: a walk of each path.  With
-        // H < 32 they build all masks too.
+        // or workgroup 0 of a rejected plan; its wave 0 jumps through LDS.  The others with tree
+        // keys need them for the tree tiles: for N <= 64 every wave works them out in registers
+        // (masks64_jump), for larger trees their wave 0 builds them in LDS too.  Pointer jumping
+        // takes log2 N rounds: a walk of each row's path took up to N dependent steps (18 us
+        // more for a 128-node chain).
         writer = ok ? unit.rt == 0 && unit.s == unit.sb - 1 : blockIdx.x == 0;
-        vis_full = writer || (unit.b >= 0 && unit.s == 0 && a.H < kRowsPerWave);
-        walk = !vis_full && unit.b >= 0 && unit.s == 0;
+        vis_full = writer || (unit.b >= 0 && unit.s == 0 && a.N > 64);
+        own = !vis_full && unit.b >= 0 && unit.s == 0;
         if (unit.b < 0) {
             wait_vm_all();          // the parents copy; no copy may still be landing when a workgroup exits
             if (vis_full && wave == 0) fused_masks_wave(fvis, a.N, a.W, a.fp.masks_out, a.fp.dev_status, lane);
@@ -1578,39 +1566,20 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     issue_first(unit);
     if constexpr (FUSED) {
         if (vis_full) {
-            // while the copies land
+            // while the copies land: the parents copy went out before the 2*NINST copies of
+            // issue_first (loads complete in order)
             if (wave == 0) {
-                wait_vm_all();
+                asm volatile("s_waitcnt vmcnt(%0)" : : "i"(2 * Dma::NINST) : "memory");
                 fused_masks_wave(fvis, a.N, a.W, writer ? a.fp.masks_out : nullptr, writer ? a.fp.dev_status : nullptr,
                                  lane);
             }
-        } else if (walk) {
-            // the masks of this wave's rows' nodes (at most two), into fvis for the tree tiles,
-            // while the copies land.  This wave's parents copy went out before its last 2*NINST
-            // copies (loads complete in order).  The two waves of a row half write the same words.
+        } else if (own) {
+            // the masks of all N <= 64 nodes (the tree tile reads word 0) while the copies land.
+            // This wave's parents copy went out before its last 2*NINST copies (loads complete in
+            // order).  Every wave writes the same words.
             asm volatile("s_waitcnt vmcnt(%0)" : : "i"(2 * Dma::NINST) : "memory");
-            // the rows' nodes as the tile loop takes them: rows past R read row R - 1
-            const int64_t r_first = row0 + (int64_t)rh * kRowsPerWave, r_last = r_first + kRowsPerWave - 1;
-            const int64_t r_lo = r_first < R ? r_first : R - 1, r_hi = r_last < R ? r_last : R - 1;
-            const int n_lo = (int)(r_lo / a.H), n_hi = (int)(r_hi / a.H);
-            if (a.N <= 64) {
-                const int par_v = fvis.par[wave][lane];
-                const uint64_t m_lo = node_mask_walk64(par_v, n_lo);
-                const uint64_t m_hi = n_hi != n_lo ? node_mask_walk64(par_v, n_hi) : m_lo;
-                if (lane < 4) fvis.msk[lane][n_lo] = lane == 0 ? m_lo : 0ull;
-                if (n_hi != n_lo && lane < 4) fvis.msk[lane][n_hi] = lane == 0 ? m_hi : 0ull;
-            } else {
-                int par_v[kMaxNodes / 64];
-#pragma unroll
-                for (int k = 0; k < kMaxNodes / 64; k++) par_v[k] = fvis.par[wave][lane + 64 * k];
-                uint64_t m[4];
-                node_mask_walk(par_v, n_lo, m);
-                if (lane < 4) fvis.msk[lane][n_lo] = lane == 0 ? m[0] : lane == 1 ? m[1] : lane == 2 ? m[2] : m[3];
-                if (n_hi != n_lo) {
-                    node_mask_walk(par_v, n_hi, m);
-                    if (lane < 4) fvis.msk[lane][n_hi] = lane == 0 ? m[0] : lane == 1 ? m[1] : lane == 2 ? m[2] : m[3];
-                }
-            }
+            const uint64_t mine = masks64_jump(fvis.par[wave][lane], a.N, lane);
+            if (lane < a.N) fvis.msk[0][lane] = mine;
         }
     }
 
