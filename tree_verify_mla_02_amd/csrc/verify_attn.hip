@@ -1148,12 +1148,20 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
             if (h == 1) __syncthreads();       // waves 0 and 1 are done reading half 0
             dq.template issue<0, Dma::NINST>();
             if constexpr (FUSED) {
-                if (h == 0 && vis_full && wave == 0) {
-                    // the masks while tile 0 and the first query rows land: the parents copy
-                    // went out before their 2 * NINST copies (loads complete in order)
+                // the masks while tile 0 and the first query rows land: the parents copy went
+                // out before their 2 * NINST copies (loads complete in order).  Up to 64 nodes
+                // every wave works them out in registers (the tree tile reads word 0); the
+                // writer and larger trees build them in LDS with wave 0.
+                const bool regs = !writer && a.N <= 64;
+                if (h == 0 && vis_full && (regs || wave == 0)) {
                     asm volatile("s_waitcnt vmcnt(%0)" : : "i"(2 * Dma::NINST) : "memory");
-                    fused_masks_wave(fvis, a.N, a.W, writer ? a.fp.masks_out : nullptr,
-                                     writer ? a.fp.dev_status : nullptr, lane);
+                    if (regs) {
+                        const uint64_t mine = masks64_jump(fvis.par[wave][lane], a.N, lane);
+                        if (lane < a.N) fvis.msk[0][lane] = mine;
+                    } else {
+                        fused_masks_wave(fvis, a.N, a.W, writer ? a.fp.masks_out : nullptr,
+                                         writer ? a.fp.dev_status : nullptr, lane);
+                    }
                 }
             }
             wait_vm_all();
