@@ -100,6 +100,10 @@ SMALL = {
                    [0, 1, 2999]),
     "t64_rows888": (workloads.Spec("t64p", 73, 2, 37, 24, 512, 64, "bf16", None, ragged=(100, 5000), tree="random",
                                    outlier_p=0.01), [5000, 777]),
+    # 128 heads (the DeepSeek-V3 count): over a short cache a 64-row tile is half of a node's
+    # heads; over a long one a 128-row tile is one node
+    "h128_t64": (workloads.Spec("h128a", 68, 1, 32, 128, 512, 64, "bf16", 3000, depth=6, topk=8), None),
+    "h128_t128": (workloads.Spec("h128b", 69, 1, 32, 128, 512, 64, "bf16", 10000, depth=6, topk=8), None),
 }
 
 
@@ -108,6 +112,16 @@ def test_small_all_rows(name):
     spec, lens = SMALL[name]
     inp = workloads.make_inputs(spec, seed=0, cache_lens=None if lens is None else np.array(lens, np.int32))
     check(name, inp)
+
+
+@pytest.mark.parametrize("name", ["split", "nodes256", "chain_short", "dec_tree60", "rows1000_long", "h128_t64",
+                                  "h128_t128"])
+def test_small_one_launch(name):
+    """The one-request cases through kdt_tree_verify_prepare_attend (masks, plan and attention in
+    one launch), every row against the oracle."""
+    spec, lens = SMALL[name]
+    inp = workloads.make_inputs(spec, seed=0, cache_lens=None if lens is None else np.array(lens, np.int32))
+    check(name + " (one launch)", inp, staged="one")
 
 
 def test_chain_equals_causal_prefill_on_gpu():
