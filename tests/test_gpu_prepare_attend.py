@@ -128,6 +128,34 @@ def test_fused_shorter_cache(base, L):
     _same(fused, staged, f"{base} L={L}")
 
 
+@pytest.mark.parametrize("base,lens", [("kimi", [4096, 100, 0, 4095, 1025, 4096]),
+                                       ("chain", [32768, 300, 0, 20000, 32767])])
+def test_fused_one_workspace_changing_lengths(base, lens):
+    """One workspace and one output buffer serve calls with changing cache_lens[0] (fewer splits,
+    no cache, back to the full length): every call equals a fresh staged call bit for bit, so
+    nothing a previous call left in the workspace (unit slots, partials of splits it had) leaks."""
+    inp = _inputs(base)
+    dev = to_device(inp)
+    maxL = int(inp.cache_lens.max())
+    desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, maxL,
+                         inp.total_len)
+    ws = torch.zeros(kdt.workspace_size(desc), dtype=torch.uint8, device="cuda")
+    out = torch.empty(dev.q_lat.shape, dtype=torch.float32, device="cuda")
+    B, N = dev.parents.shape
+    masks = torch.empty((B, N, (N + 63) // 64), dtype=torch.int64, device="cuda")
+    for L in lens:
+        lt = torch.tensor([L], dtype=torch.int32, device="cuda")
+        out.fill_(float("nan"))
+        kdt.prepare_attend(dev.parents, lt, dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope,
+                           inp.scale, out, desc, ws, masks_out=masks)
+        kdt.combine(out, desc, ws)
+        torch.cuda.synchronize()
+        staged = _run(inp, dev, lt, fused=False, max_len=maxL)
+        assert torch.equal(masks.cpu(), staged[0]), f"{base} L={L}: masks differ"
+        assert torch.equal(out.cpu().view(torch.int32), staged[1].view(torch.int32)), f"{base} L={L}: outputs differ"
+        print(f"PASS {base} L={L}: reused workspace equals a fresh staged call", flush=True)
+
+
 @pytest.mark.parametrize("base,L", [("kimi", 4097), ("kimi", -1), ("chain", 32769), ("chain", -1)])
 def test_fused_rejected_cache_len(base, L):
     """A length outside [0, max_cache_len]: KDT_DEV_CACHE_LEN, outputs untouched, masks still
