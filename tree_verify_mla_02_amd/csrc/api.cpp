@@ -80,6 +80,9 @@ int check_desc(const kdt_verify_desc *d) {
     if (d->max_cache_len < 0 || d->total_cache_len < 0)
         return fail(KDT_ERR_INVALID_ARG, "cache length bounds must be >= 0");
     if (d->max_cache_len > (int64_t)INT32_MAX) return fail(KDT_ERR_INVALID_ARG, "max_cache_len exceeds int32");
+    // 32-bit key arithmetic of the plan: a split count is (L + tree places + chunk - 1) / chunk
+    if (d->max_cache_len > ((int64_t)1 << 30))
+        return fail(KDT_ERR_UNSUPPORTED, "max_cache_len above 2^30 keys is not supported");
     const int64_t epc = 16 / elem_size(d->dtype);
     const struct { int64_t stride; int width; const char *name; } s[] = {
         {d->q_lat_stride, d->d_latent, "q_lat_stride"},   {d->q_rope_stride, d->d_rope, "q_rope_stride"},
@@ -135,6 +138,7 @@ kdt::AttnArgs make_args(const kdt_verify_desc &d, const kdt::Geometry &g, void *
     a.tile_rows = g.tile_rows;
     a.S = g.nsplit;
     a.chunk = g.chunk;
+    a.tree_keys = g.tree_keys;
     a.hdr = (const kdt::WsHeader *)(w + g.off_header);
     a.offsets = (const int64_t *)(w + g.off_offsets);
     a.lens = (const int32_t *)(w + g.off_lens);
@@ -173,23 +177,31 @@ bool make_geometry(const kdt_verify_desc &d, int num_cus, Geometry *g) {
     x.mask_words = (d.num_nodes + 63) / 64;
     const int64_t units0 = (int64_t)d.batch * rt;
     const int64_t maxL = d.max_cache_len;
-    // Split the committed keys only when the batch alone cannot fill the GPU (about two
-    // workgroups per CU); keep every split at least kMinChunk keys so partials stay small
-    // next to the key traffic.
+    // Split the keys only when the batch alone cannot fill the GPU (about two workgroups per
+    // CU); keep every split at least kMinChunk keys so partials stay small next to the key
+    // traffic.  Split 0 also does the tree's tiles.  A tree of more than one 64-key tile takes
+    // Tf = tree_span(N) places in the split range, so that split 0 does no more tiles than the
+    // others (a 256-node prefill chunk over 4096 keys: 34 tiles on the longest split against 36,
+    // 6 % less time).  A one-tile tree takes none: a place for it measured 1.5-2.7 % slower on
+    // the Kimi, 16-node chain and 7-node shapes (2 % faster on a one-node decode step).
+    const int64_t T = d.num_nodes > kKeysPerTile ? tree_span(d.num_nodes) : 0;
+    const int64_t Lv = maxL + T;
     int64_t S = 1;
     if (units0 < 2 * (int64_t)num_cus && maxL > kMinChunk) {
         const int64_t want = ((int64_t)num_cus + units0 - 1) / units0;
-        const int64_t cap = (maxL + kMinChunk - 1) / kMinChunk;
+        const int64_t cap = (Lv + kMinChunk - 1) / kMinChunk;
         S = want < cap ? want : cap;
         if (S < 1) S = 1;
     }
-    int64_t chunk = maxL > 0 ? (maxL + S - 1) / S : kKeysPerTile;
+    int64_t chunk = Lv > 0 ? (Lv + S - 1) / S : kKeysPerTile;
     chunk = (chunk + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
     if (chunk < kKeysPerTile) chunk = kKeysPerTile;
-    S = maxL > 0 ? (maxL + chunk - 1) / chunk : 1;
+    if (chunk < T) chunk = T;                 // the tree's places fit in split 0
+    S = Lv > 0 ? (Lv + chunk - 1) / chunk : 1;
     if (S < 1) S = 1;
     x.nsplit = (int)S;
     x.chunk = chunk;
+    x.tree_keys = (int)T;
     // Units are dealt to the 8 XCD lanes of the grid in groups of bt row tiles x bs splits of
     // one request; the row tiles of a group share its splits' keys through one L2, its splits
     // share the row tiles' queries.  By default a group is one split with all RT row tiles.

@@ -12,8 +12,13 @@ namespace kdt {
 
 // Work decomposition of the verify attention.
 //   A work unit is (request b, row tile rt, key split s).  A row tile is 128 query rows
-//   (4 waves x 32 rows, rows node-major r = i*H + h); a key split is a contiguous range of
-//   `chunk` committed-cache keys.  Split 0 of every request also owns its tree segment.
+//   (4 waves x 32 rows, rows node-major r = i*H + h).  Split 0 of every request also owns its
+//   tree segment.  The keys of a request are split as one range of L + Tf "virtual" keys, Tf
+//   committed-key places given to the tree, then its L committed-cache keys: split s takes
+//   virtual keys [s*chunk, (s+1)*chunk), that is cache keys [s*chunk - Tf, (s+1)*chunk - Tf)
+//   (from 0 for split 0).  Tf = tree_span(N) for trees of more than one 64-key tile, so that
+//   split 0, tree included, does no more tiles than the others; 0 for one-tile trees, whose
+//   tile split 0 does on top of its share (chunk >= Tf always).
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerTile = kWaves * kRowsPerWave;   // 128
@@ -27,13 +32,17 @@ static_assert(kMinChunk % 64 == 0 && kMinChunk >= 64, "whole key tiles per split
 constexpr int kMaxTreeTable = 8192;                    // tree builder: D * K log probabilities in LDS
 constexpr int kXcds = 8;                               // MI355X: 8 XCDs, each with its own L2
 
+// Keys of the tree segment as the attention takes them: whole 64-key tiles.
+constexpr int64_t tree_span(int N) { return (int64_t)kKeysPerTile * ((N + kKeysPerTile - 1) / kKeysPerTile); }
+
 struct Geometry {
     int64_t rows;          // R = N * H query rows per request
     int tile_rows;         // query rows per workgroup: 128, or 64 for small requests (see make_geometry)
     int row_tiles;         // RT = ceil(R / tile_rows): row tiles of the unit list
     int layout_tiles;      // ceil(R / 128): 128-row tiles of the split-partial layout
     int nsplit;            // S: splits per request at most (1 = no split)
-    int64_t chunk;         // committed keys per split
+    int64_t chunk;         // virtual keys (tree places, then committed keys) per split
+    int tree_keys;         // Tf: committed-key places the tree takes in split 0
     int64_t units;         // grid size of the attention kernel: 8 * ceil(G / 8) * bt * bs slots
     int bt, bs;            // a plan group: bt row tiles x bs splits of one request
     int64_t groups;        // G = B * ceil(RT / bt) * ceil(S / bs)
@@ -96,6 +105,7 @@ struct AttnArgs {
     int RT, S;             // RT: 128-row tiles of the partial layout
     int tile_rows;         // 128: verify_attn_kernel; 64: the 64-row kernel (unit rt counts 64-row tiles)
     int64_t chunk;
+    int tree_keys;         // Tf (see above)
     float scale_log2;      // scale * log2(e): scores are kept in the base-2 domain
     const WsHeader *hdr;
     const int64_t *offsets;

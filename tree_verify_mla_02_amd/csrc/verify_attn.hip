@@ -58,11 +58,11 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
-// Splits used for request b: split 0 always exists (it owns the tree keys).
-__device__ __forceinline__ int splits_of(int L, int64_t chunk, int S) {
-    if (L <= 0) return 1;
-    const int64_t n = (L + chunk - 1) / chunk;
-    return (int)(n < S ? n : S);
+// Splits used for request b: those that cut its Tf + L virtual keys (Tf committed-key places
+// given to the tree; see kdt_internal.h).  Split 0 always exists (it owns the tree keys).
+__device__ __forceinline__ int splits_of(int L, int Tf, int64_t chunk, int S) {
+    const int64_t n = ((L > 0 ? L : 0) + Tf + chunk - 1) / chunk;
+    return (int)(n < 1 ? 1 : n < S ? n : S);
 }
 
 // ------------------------------------------------------------------------------ plan
@@ -98,6 +98,7 @@ struct PlanArgs {
     int B, N;
     int64_t max_len, total_len;
     int RT, S, bt, bs;
+    int tree_keys;         // Tf: committed-key places of the tree in split 0
     int64_t chunk, U;
     WsHeader *hdr;
     int64_t *offsets;
@@ -144,11 +145,12 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, PlanLds &L) {
     const bool req_lds = B <= kMaxLdsReq;
     int32_t *lens = req_lds ? L.lens : pa.lens;
     int64_t *offs = req_lds ? L.offs : pa.offsets;
-    // splits of a request of len keys: ceil(len / chunk), at least 1, at most S
+    // virtual keys before the committed ones: the tree's places (0 or its whole tiles)
+    const uint32_t T = (uint32_t)pa.tree_keys;
+    // splits of a request of len committed keys: ceil((len + T) / chunk), at least 1, at most S
     auto splits = [&](int len) {
-        if (len <= 0) return 1;
-        const uint32_t n = fdiv((uint32_t)len + chunk - 1u, pa.fd_chunk);   // < 2^32
-        return (int)(n < (uint32_t)S ? n : (uint32_t)S);
+        const uint32_t n = fdiv((uint32_t)(len > 0 ? len : 0) + T + chunk - 1u, pa.fd_chunk);   // < 2^32
+        return (int)(n < 1u ? 1u : n < (uint32_t)S ? n : (uint32_t)S);
     };
     if (tid == 0) L.ok = 1;
     lds_sync();
@@ -207,8 +209,9 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, PlanLds &L) {
     if (req_lds) lds_sync(); else __syncthreads();
     const int ok = L.ok;
     // Groups: bt row tiles x bs splits of one request, (request, row-tile block, split block)
-    // with the split block fastest.  A group's work is the keys of its splits (its row tiles
-    // all cost the same).  With G <= kMaxSortGroups groups are ranked by a unique 32-bit key:
+    // with the split block fastest.  A group's work is the virtual keys of its splits, plus the
+    // N tree keys for split 0 when they have no place among them (its row tiles all cost the
+    // same).  With G <= kMaxSortGroups groups are ranked by a unique 32-bit key:
     // bit 31 = the group has a split (a request's lengths may leave a split block empty, and
     // rejected lengths leave every group empty), bits 30..11 = its 64-key tiles (saturated),
     // bits 10..0 = 2047 - g (ties by index).  Larger keys go first.
@@ -225,9 +228,10 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, PlanLds &L) {
             int64_t w = -1;
             if (ok) {
                 const int sbr = req_lds ? L.sb[b] : splits(len);
+                const int64_t lv = (int64_t)(len > 0 ? len : 0) + T;
                 for (int sp = gs * bs; sp < gs * bs + bs && sp < sbr; sp++) {
-                    const int64_t left = (int64_t)len - (int64_t)sp * chunk;
-                    w = (w < 0 ? 0 : w) + (left < chunk ? (left > 0 ? left : 0) : chunk) + (sp == 0 ? N : 0);
+                    const int64_t left = lv - (int64_t)sp * chunk;
+                    w = (w < 0 ? 0 : w) + (left < chunk ? (left > 0 ? left : 0) : chunk) + (sp == 0 && T == 0u ? N : 0);
                 }
             }
             const int64_t tiles = w < 0 ? 0 : (w + kKeysPerTile - 1) / kKeysPerTile;
@@ -283,9 +287,11 @@ __device__ __forceinline__ void plan_body(const PlanArgs &pa, PlanLds &L) {
             const int len = lens[b];
             const int sb = req_lds ? L.sb[b] : splits(len);
             if (rt < RT && sp < sb) {
-                const int64_t k0 = (int64_t)sp * chunk;
-                const int64_t k1 = k0 + chunk < (int64_t)len ? k0 + chunk : (int64_t)len;
-                un = Unit{b, rt, sp, sb, (int32_t)k0, (int32_t)k1, offs[b] + k0};
+                // committed keys [k0, k1): virtual [sp*chunk, (sp+1)*chunk) less the tree's places
+                const int64_t v0 = (int64_t)sp * chunk - T, v1 = v0 + chunk;
+                const int64_t k0 = v0 > 0 ? v0 : 0;
+                const int64_t k1 = v1 < (int64_t)len ? v1 : (int64_t)len;
+                un = Unit{b, rt, sp, sb, (int32_t)k0, (int32_t)(k1 > k0 ? k1 : k0), offs[b] + k0};
             }
         }
         pa.units[u] = un;
@@ -857,15 +863,18 @@ __device__ __forceinline__ float4 load_part4(const uint32_t *src) {
 // Work unit the plan kernel gives grid slot u when the batch is one request of L committed
 // keys (plan_body with B = 1).  The plan ranks its groups by work, longest first, ties by
 // index.  With one request a group's work depends only on its split block gs and never grows
-// with gs: block 0 holds split 0 and the tree keys, then come the blocks whose bs splits are
-// all full, then at most one partly filled block, then blocks past the last split.  So the
-// groups of equal work form runs of consecutive gs, and within a run the plan's order is the
-// index order (row block major).  Slot -> rank p follows the plan's snake dealing; rank p lies
-// in the run that contains gs = p / GR.
+// with gs.  When the tree has Tf places in the split range (see kdt_internal.h) the blocks whose
+// bs splits are all full come first, block 0 among them; with none, block 0 (its tree keys on
+// top of its share) comes alone before them.  Then come at most one partly filled block, then
+// the blocks past the last split.  So the groups of equal work form runs of consecutive gs, and
+// within a run the plan's order is the index order (row block major).  Slot -> rank p follows
+// the plan's snake dealing; rank p lies in the run that contains gs = p / GR.
 // Branch-free, so that the kernel-argument loads it needs go out together at the start.
-__device__ __forceinline__ Unit fused_unit(const FusedPlan &f, int64_t chunk, int S, int L, uint32_t u) {
-    // splits_of without its 64-bit division: L + chunk - 1 < 2^32 (both below 2^31 + 64)
-    const uint32_t nsp = fdiv((uint32_t)(L > 0 ? L : 1) + (uint32_t)chunk - 1u, f.fd_chunk);
+__device__ __forceinline__ Unit fused_unit(const FusedPlan &f, int64_t chunk, int S, int Tf, int L, uint32_t u) {
+    // splits_of without its 64-bit division: lv + chunk - 1 < 2^32 (the host bounds the cache
+    // length by 2^30 keys)
+    const int64_t lv = (int64_t)(L > 0 ? L : 0) + Tf;
+    const uint32_t nsp = fdiv((uint32_t)(lv > 0 ? lv : 1) + (uint32_t)chunk - 1u, f.fd_chunk);
     const int sb = nsp < (uint32_t)S ? (int)nsp : S;
     const uint32_t x = u & (kXcds - 1), k = u >> 3;       // kXcds = 8
     const uint32_t round = fdiv(k, f.fd_per);
@@ -873,13 +882,14 @@ __device__ __forceinline__ Unit fused_unit(const FusedPlan &f, int64_t chunk, in
     const uint32_t p = round * kXcds + ((round & 1) ? kXcds - 1 - x : x);
     const int E = (int)fdiv((uint32_t)(sb + f.bs - 1), f.fd_bs);     // blocks with a split
     const int c = (int)fdiv(p, f.fd_gr);
-    // blocks 1 .. E-1 (E >= 2 when 0 < c < E): block E-1 holds L - (E-1)*span keys, at least 1
-    // and at most span, as many 64-key tiles as a full block when more than span - 64
+    // blocks 0 .. E-2 are full; block E-1 holds lv - (E-1)*span virtual keys, at least 1 and at
+    // most span, as many 64-key tiles as a full block when more than span - 64.  With Tf = 0
+    // block 0 is a run of its own.
     const int64_t span = (int64_t)f.bs * chunk;           // a multiple of 64
-    const int fe = (L - (int64_t)(E - 1) * span > span - kKeysPerTile) ? E - 1 : E - 2;   // last full block
-    const bool mid = c > 0 && c < E, in_full = c <= fe;
-    const int lo = c == 0 ? 0 : mid ? (in_full ? 1 : E - 1) : E;
-    const int hi = c == 0 ? 0 : mid ? (in_full ? fe : E - 1) : f.GS - 1;
+    const int fe = (lv - (int64_t)(E - 1) * span > span - kKeysPerTile) ? E - 1 : E - 2;   // last full block
+    const bool alone = Tf == 0, first = alone && c == 0, in_full = c <= fe, mid = c < E;
+    const int lo = first ? 0 : in_full ? (alone ? 1 : 0) : mid ? E - 1 : E;
+    const int hi = first ? 0 : in_full ? fe : mid ? E - 1 : f.GS - 1;
     const uint32_t m = (uint32_t)(hi - lo + 1), q = p - (uint32_t)f.GR * (uint32_t)lo;
     // q / m through a float reciprocal: q < G <= 2048, so the estimate is off by at most one
     uint32_t gr = (uint32_t)((float)q * __builtin_amdgcn_rcpf((float)m));
@@ -888,8 +898,11 @@ __device__ __forceinline__ Unit fused_unit(const FusedPlan &f, int64_t chunk, in
     const uint32_t gs = (uint32_t)lo + (q - gr * m);
     const uint32_t ib = fdiv(i, f.fd_bs);
     const int rt = (int)(gr * (uint32_t)f.bt + ib), sp = (int)(gs * (uint32_t)f.bs + (i - ib * (uint32_t)f.bs));
-    const int64_t k0 = (int64_t)sp * chunk;
-    const int64_t k1 = k0 + chunk < (int64_t)L ? k0 + chunk : (int64_t)L;
+    // committed keys [k0, k1): virtual [sp*chunk, (sp+1)*chunk) less the tree's places
+    const int64_t v0 = (int64_t)sp * chunk - Tf, v1 = v0 + chunk;
+    const int64_t k0 = v0 > 0 ? v0 : 0;
+    const int64_t k1e = v1 < (int64_t)L ? v1 : (int64_t)L;
+    const int64_t k1 = k1e > k0 ? k1e : k0;
     const bool valid = p < (uint32_t)f.G && rt < f.RT && sp < sb;
     return valid ? Unit{0, rt, sp, sb, (int32_t)k0, (int32_t)k1, k0} : Unit{-1, 0, 0, 0, 0, 0, 0};
 }
@@ -1045,7 +1058,7 @@ __global__ __launch_bounds__(256, 1) void verify_attn_kernel(AttnArgs a) {
         fused_parents_copy(fvis.par[wave], a.fp.parents, a.N, lane);
         const int L = a.fp.cache_lens[0];
         const bool ok = L >= 0 && (int64_t)L <= a.fp.max_len && (int64_t)L <= a.fp.total_len;
-        unit = ok ? fused_unit(a.fp, a.chunk, a.S, L, blockIdx.x) : Unit{-1, 0, 0, 0, 0, 0, 0};
+        unit = ok ? fused_unit(a.fp, a.chunk, a.S, a.tree_keys, L, blockIdx.x) : Unit{-1, 0, 0, 0, 0, 0, 0};
         if (threadIdx.x == 0) {
             a.fp.units[blockIdx.x] = unit;
             if (blockIdx.x == 0) {
@@ -1506,7 +1519,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
         // the plan, for this workgroup's slot only (one request: cache_lens[0] is all it reads)
         const int L = a.fp.cache_lens[0];
         const bool ok = L >= 0 && (int64_t)L <= a.fp.max_len && (int64_t)L <= a.fp.total_len;
-        unit = ok ? fused_unit(a.fp, a.chunk, a.S, L, blockIdx.x) : Unit{-1, 0, 0, 0, 0, 0, 0};
+        unit = ok ? fused_unit(a.fp, a.chunk, a.S, a.tree_keys, L, blockIdx.x) : Unit{-1, 0, 0, 0, 0, 0, 0};
         if (threadIdx.x == 0) {
             a.fp.units[blockIdx.x] = unit;
             if (blockIdx.x == 0) {
@@ -1805,7 +1818,7 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
         }
     }
     const int ok = a.hdr->ok;
-    const int sb = splits_of(a.lens[b], a.chunk, a.S);
+    const int sb = splits_of(a.lens[b], a.tree_keys, a.chunk, a.S);
     if (!ok || sb <= 1) return;                       // uniform over the workgroup
     float acc[GC][4];
 #pragma unroll
@@ -1899,6 +1912,7 @@ static PlanArgs plan_args(const int32_t *cache_lens, const kdt_verify_desc &d, c
     pa.bt = g.bt;
     pa.bs = g.bs;
     pa.chunk = g.chunk;
+    pa.tree_keys = g.tree_keys;
     pa.U = g.units;
     pa.hdr = (WsHeader *)(w + g.off_header);
     pa.offsets = (int64_t *)(w + g.off_offsets);
@@ -1961,7 +1975,7 @@ bool fused_supported(const kdt_verify_desc &d, const Geometry &g) {
     // and work keys that do not saturate (fewer than 0xfffff tiles per group)
     return d.batch == 1 && d.dtype == KDT_BF16 && d.d_latent == 512 && d.d_rope == 64 &&
            g.groups <= kMaxSortGroups && g.units <= INT32_MAX &&
-           d.max_cache_len + d.num_nodes < (int64_t)0xfffff * kKeysPerTile;
+           d.max_cache_len + tree_span(d.num_nodes) < (int64_t)0xfffff * kKeysPerTile;
 }
 
 hipError_t launch_attend_fused(AttnArgs a, const kdt_verify_desc &d, const Geometry &g, const int32_t *parents,
