@@ -49,16 +49,18 @@ def to_device(inp: workloads.Inputs) -> DevInputs:
                      q_rope=inp.q_rope.cuda(), kv=kv.cuda(), tree_kv=inp.tree_kv.cuda(), dc=inp.spec.d_latent)
 
 
-def run_gpu(inp: workloads.Inputs, dev: DevInputs = None, staged=False):
+def run_gpu(inp: workloads.Inputs, dev: DevInputs = None, staged=False, max_len=None):
     """Masks [B,N,W] (numpy uint64) and outputs [B,N,H,d_c] (torch fp32, on device).
 
     staged: False = kdt_build_visibility + kdt_tree_verify_attn; True = visibility, plan,
     attend, combine as separate calls; "prepare" = kdt_tree_verify_prepare (masks and plan
     in one launch), attend, combine; "one" = kdt_tree_verify_prepare_attend (masks, plan and
-    attention in one launch where the batch allows), combine."""
+    attention in one launch where the batch allows), combine.  max_len: the cache-length bound
+    the geometry is made for (default: the longest request)."""
     dev = dev or to_device(inp)
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     maxL = int(inp.cache_lens.max()) if inp.cache_lens.numel() else 0
+    maxL = maxL if max_len is None else max_len
     total = inp.total_len
     if staged == "one":
         desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, maxL, total)

@@ -45,6 +45,8 @@ KERNELS = {
     "k128": workloads.Spec("e128", 70, 1, 16, 64, 512, 64, "bf16", 9000, tree="random"),
     "k64": workloads.Spec("e64", 71, 1, 2, 64, 512, 64, "bf16", 1300, tree="chain"),
     "k64w": workloads.Spec("e64w", 75, 1, 16, 64, 512, 64, "bf16", 1500, tree="random"),
+    # a two-tile tree: its 128 keys have places in the split range (14 splits of 384 keys)
+    "k64p": workloads.Spec("e64p", 77, 1, 128, 8, 512, 64, "bf16", 5000, tree="random"),
     "bf16s": workloads.Spec("es", 72, 2, 9, 8, 64, 16, "bf16", 700, tree="random"),
     "f32": workloads.Spec("ef", 73, 2, 8, 4, 64, 16, "f32", 700, tree="random"),
 }
@@ -57,6 +59,25 @@ def test_k128_takes_128_row_tiles():
     dev = to_device(inp)
     desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, 9000, inp.total_len)
     assert kdt.num_splits(desc) == 29
+
+
+def test_two_tile_tree_has_places_in_the_split_range():
+    """k64p's 128-node tree takes 128 places in the range the splits cut: 5128 virtual keys in 14
+    splits of 384 (split 0: the tree tiles and committed keys 0..255).  Without places the 5000
+    committed keys would make 16 splits of 320."""
+    inp = workloads.make_inputs(KERNELS["k64p"], seed=0)
+    dev = to_device(inp)
+    desc = kdt.make_desc(dev.q_lat, dev.q_rope, dev.ckv, dev.krope, dev.tree_ckv, dev.tree_krope, 5000, inp.total_len)
+    assert kdt.num_splits(desc) == 14
+
+
+@pytest.mark.parametrize("L", [255, 256, 257, 4480, 4999])
+def test_two_tile_tree_split_boundaries_vs_oracle(L):
+    """Cache lengths at the edges of split 0's committed keys (256) and of the last split, under the
+    geometry made for 5000 keys: every row against the oracle, and the one-launch call equal to the
+    staged calls."""
+    inp = workloads.make_inputs(KERNELS["k64p"], seed=9, cache_lens=np.array([L], dtype=np.int32))
+    _gpu_vs_oracle(f"k64p L={L} vs oracle", inp, max_len=5000)
 
 
 def _cast(x: np.ndarray, like: torch.Tensor) -> torch.Tensor:
@@ -79,11 +100,12 @@ def _paths(parents: np.ndarray):
     return out
 
 
-def _gpu_vs_oracle(name, inp, tol=None):
+def _gpu_vs_oracle(name, inp, tol=None, max_len=None):
     """Every row of the GPU output against the oracle; returns (gpu out, oracle out) as fp64.
     A one-request bf16 512 + 64 batch also runs through the one-launch call, which must give the
-    staged calls' bits."""
-    _, out, status = run_gpu(inp)
+    staged calls' bits.  max_len: the cache-length bound of the geometry (default: the longest
+    request)."""
+    _, out, status = run_gpu(inp, max_len=max_len)
     assert status == 0
     got = out.cpu().double().numpy()
     ref = oracle.run(inp)[1]
@@ -95,8 +117,8 @@ def _gpu_vs_oracle(name, inp, tol=None):
     sp = inp.spec
     if sp.batch == 1 and sp.dtype == "bf16" and sp.d_latent == 512:
         dev = to_device(inp)
-        _, staged, _ = run_gpu(inp, dev, staged="prepare")
-        _, one, st1 = run_gpu(inp, dev, staged="one")
+        _, staged, _ = run_gpu(inp, dev, staged="prepare", max_len=max_len)
+        _, one, st1 = run_gpu(inp, dev, staged="one", max_len=max_len)
         assert st1 == 0
         assert torch.equal(one.view(torch.int32), staged.view(torch.int32)), f"{name}: one launch differs"
         print(f"PASS {name}: one launch bit-identical to the staged calls", flush=True)

@@ -116,7 +116,11 @@ def test_fused_against_oracle_kimi():
 
 
 @pytest.mark.parametrize("base,L", [("kimi", L) for L in (0, 1, 63, 64, 65, 1000, 1024, 1025, 4095)] +
-                         [("chain", L) for L in (0, 1, 1023, 1025, 20000, 32767)])
+                         [("chain", L) for L in (0, 1, 1023, 1025, 20000, 32767)] +
+                         # trees with places in the split range: split 0 = the tree's 128 (256) keys
+                         # then committed keys [0, 4032) ([0, 1920)), split 1 the rest
+                         [("chain128", L) for L in (0, 1, 4031, 4032, 4033, 8191)] +
+                         [("prefill4k", L) for L in (0, 1919, 1920, 1921, 4095)])
 def test_fused_shorter_cache(base, L):
     """cache_lens[0] below the bound the geometry was made for: fewer splits, partial splits."""
     inp = _inputs(base)
@@ -129,7 +133,8 @@ def test_fused_shorter_cache(base, L):
 
 
 @pytest.mark.parametrize("base,lens", [("kimi", [4096, 100, 0, 4095, 1025, 4096]),
-                                       ("chain", [32768, 300, 0, 20000, 32767])])
+                                       ("chain", [32768, 300, 0, 20000, 32767]),
+                                       ("chain128", [8192, 4032, 0, 4033, 8192])])
 def test_fused_one_workspace_changing_lengths(base, lens):
     """One workspace and one output buffer serve calls with changing cache_lens[0] (fewer splits,
     no cache, back to the full length): every call equals a fresh staged call bit for bit, so
