@@ -42,6 +42,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -655,6 +656,7 @@ struct BlockSm {
             }
         }
     }
+
 };
 
 // Compile-time placement of items [LO, HI) into the steps of a pipeline: item LO + n goes to
@@ -1428,6 +1430,75 @@ __device__ __forceinline__ void qk_block(const LDS_AS char *const (&pq)[Sh::CB /
     });
 }
 
+// S^T of the same block with MFMA 16x16x32, in two 16-key halves of two 16-row blocks.  A
+// 16x16x32 MFMA gives lane l the keys 4*(l/16) + i (i = 0..3) of a half for query row l % 16 of
+// a row block: the wave's 32 rows are two row blocks, two accumulators sharing each K fragment.
+// With the half's keys taken in the A operand with bits 2 and 3 swapped, the four lane groups
+// hold keys 0-3, 8-11, 4-7 and 12-15, and one v_permlane16_swap of the two row blocks'
+// registers (odd 16-lane rows of the first operand exchanged with even rows of the second)
+// leaves every lane its row l % 32 and keys 8*(i/4) + 4*(l/32) + i%4: the 32x32x16 chain's
+// layout, with the same scores bit for bit (checked on the GPU on the Kimi, decode, 7-node,
+// outlier and ragged shapes).  Used for long key splits, where it measured faster (a Kimi-shape launch, 16 tiles
+// per workgroup: 51.4 against 52.3 us); on 4-tile splits (a decode step, the 7-node block) the
+// 32x32x16 chain measured faster (21.7 against 22.2 us).  Running the next half's softmax
+// steps in this chain's shadow measured slower than both: a 16-cycle MFMA leaves too few issue
+// slots for them.
+
+// The VGPR-accumulator MFMA of this chain (see the S^T chain above for why asm).  A chain
+// alternating two accumulators needs no wait states between MFMAs; WAIT < 0: no LDS wait.
+template <int WAIT, bool FIRST>
+__device__ __forceinline__ void mfma16_s(f32x4 &acc, const bf16x8 &a, const bf16x8 &b) {
+    if constexpr (FIRST && WAIT >= 0)
+        asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, 0"
+                     : "=&v"(acc) : "v"(a), "v"(b), "i"(WAIT));
+    else if constexpr (FIRST)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+    else if constexpr (WAIT >= 0)
+        asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                     : "+v"(acc) : "v"(a), "v"(b), "i"(WAIT));
+    else
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// Both halves in one chain of 2*NQ MFMAs: per 32-dim step g of half h, row block 0 then 1 on
+// the K fragment of (h, g) (q[2g + rb]); fragments are read QD steps ahead across the half
+// boundary.  The scores land in s as the 32x32x16 chain leaves them; a VALU instruction may
+// read a 16x16x32 result 8 wait states after the MFMA, 10 are spelled out.
+template <class Sh, int NQ>
+__device__ __forceinline__ void qk16_block(const LDS_AS char *const (&pk)[2][2], const bf16x8 (&q)[NQ],
+                                           f32x16 &s) {
+    constexpr int NG = NQ / 2, NT = 2 * NG;
+    constexpr int QD = 5, NS = QD + 1;
+    static_assert(NQ % 2 == 0 && NG > QD, "whole 32-dim steps, more than the read-ahead");
+    bf16x8 kf[NS];
+    f32x4 acc[2][2];                    // [half][row block]
+    auto read = [&](auto F_) {
+        constexpr int f = decltype(F_)::value, h = f / NG, g = f % NG;
+        ds_read_k<(g / 2) * 1024>(kf[f % NS], pk[h][g % 2]);
+    };
+    static_for<0, QD>(read);
+    static_for<0, NT>([&](auto F_) {
+        constexpr int f = decltype(F_)::value, h = f / NG, g = f % NG;
+        constexpr int issued = (f + QD < NT) ? f + QD : NT;      // fragments read before step f
+        mfma16_s<issued - f - 1, g == 0>(acc[h][0], kf[f % NS], q[2 * g]);
+        // the slot step f-1 read: its last reader was the MFMA before the one just issued
+        if constexpr (f + QD < NT) read(IntC<f + QD>{});
+        __builtin_amdgcn_sched_barrier(0);
+        mfma16_s<-1, g == 0>(acc[h][1], kf[f % NS], q[2 * g + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    asm volatile("s_nop 7\n\ts_nop 1" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[h][0][i]),
+                                                            __float_as_uint(acc[h][1][i]), false, false);
+            s[8 * h + i] = __uint_as_float(x[0]);
+            s[8 * h + 4 + i] = __uint_as_float(x[1]);
+        }
+}
+
 // O^T += V^T P^T over one 32-key block: 2 x 16-key steps x NT16 column tiles x (hi, lo) = 4*NT16
 // MFMAs; vbuf already points at the wave's block.  fill(m) runs after MFMA m.  The column tiles
 // are taken rotated by NT16/2 when `rot` is the byte distance between column tiles 0 and NT16/2
@@ -1472,7 +1543,7 @@ __device__ __forceinline__ void pv_block(const LDS_AS char *vbuf, int rot, const
     });
 }
 
-template <int DC, int DR, bool FUSED = false>
+template <int DC, int DR, bool FUSED = false, bool QK16 = false>
 __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     using T = __bf16;
     using Sh = Shape<T, DC, DR>;
@@ -1606,9 +1677,23 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
 
     constexpr int QK_PAT = Sh::CB / 2;
     constexpr int PV_PAT = Sh::CB / 4;
-    int qk_base[QK_PAT], pv_base[PV_PAT][2];
+    // K and Q reads: 32x32x16 chain, lane l reads key (row) l % 32 at 16-byte chunk 2kk + l/32
+    // for 16-dim step kk; 16x16x32 chain (qk16_block), lane l reads key l % 16 with bits 2 and
+    // 3 swapped (Q: row 16*rb + l % 16 of row block rb) at chunk 4g + l/16 for 32-dim step g
+    int qk_base[QK_PAT], k16_base[2], q16_base[2][2], pv_base[PV_PAT][2];
+    if constexpr (QK16) {
+        const int kperm = (lane & 3) | ((lane & 4) << 1) | ((lane & 8) >> 1);
 #pragma unroll
-    for (int j = 0; j < QK_PAT; j++) qk_base[j] = lds_off<Sh>(lane & 31, 2 * j + half);
+        for (int j = 0; j < 2; j++) {
+            k16_base[j] = lds_off<Sh>(kperm, 4 * j + ((lane >> 4) & 3));
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++)
+                q16_base[rb][j] = lds_off<Sh>(16 * rb + (lane & 15), 4 * j + ((lane >> 4) & 3));
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < QK_PAT; j++) qk_base[j] = lds_off<Sh>(lane & 31, 2 * j + half);
+    }
     {
         const int w = 4 * half + ((lane & 15) >> 2);
         const int y = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
@@ -1621,14 +1706,17 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
     // key half 1 takes its column tiles rotated by NT16/2 (see the epilogue)
     const int rot = kh * (2 * NT16 / Sh::CB) * 1024;
 
-    bf16x8 q[NQ];
+    bf16x8 q[NQ];                       // 16x16x32 chain: q[2g + rb] for row block rb, 32-dim step g
     wait_vm_all();
     __syncthreads();
     {
         const LDS_AS char *src = qbuf + key_off<Sh>(32 * rh);
 #pragma unroll
-        for (int kk = 0; kk < NQ; kk++)
-            q[kk] = *(const LDS_AS bf16x8 *)(src + qk_base[kk % QK_PAT] + (kk / QK_PAT) * 1024);
+        for (int kk = 0; kk < NQ; kk++) {
+            const int g = kk / 2, rb = kk % 2;
+            q[kk] = QK16 ? *(const LDS_AS bf16x8 *)(src + q16_base[rb][g % 2] + (g / 2) * 1024)
+                         : *(const LDS_AS bf16x8 *)(src + qk_base[kk % QK_PAT] + (kk / QK_PAT) * 1024);
+        }
     }
     float c_pos = a.scale_log2;
     if (c_pos <= 0.f) {
@@ -1673,11 +1761,21 @@ __global__ __launch_bounds__(256, 1) void decode_attn_kernel(AttnArgs a) {
         Dma dn;
         dma_setup(dn, more ? t + 1 : t, (t + 1) & 1);
 
-        const LDS_AS char *pq[QK_PAT];
-#pragma unroll
-        for (int j = 0; j < QK_PAT; j++) pq[j] = buf + blk_off + qk_base[j];
         BlockSm bs;
-        qk_block<Sh, NQ>(pq, q, bs.s);
+        if constexpr (QK16) {
+            const LDS_AS char *pk[2][2];
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                pk[0][j] = buf + blk_off + k16_base[j];
+                pk[1][j] = pk[0][j] + key_off<Sh>(16);
+            }
+            qk16_block<Sh, NQ>(pk, q, bs.s);
+        } else {
+            const LDS_AS char *pq[QK_PAT];
+#pragma unroll
+            for (int j = 0; j < QK_PAT; j++) pq[j] = buf + blk_off + qk_base[j];
+            qk_block<Sh, NQ>(pq, q, bs.s);
+        }
         if (need_mask) mask_scores(bs.s, wv);
         // the first half of the softmax (maxima, reference, keys 0..15) before the P.V chain;
         // keys 16..31 are only read from MFMA 2*NT16 on, so their steps go into the chain
@@ -1949,6 +2047,12 @@ hipError_t launch_prepare(const int32_t *parents, uint64_t *masks, const int32_t
     return hipGetLastError();
 }
 
+// The 64-row kernel's S^T chain: 16x16x32 MFMAs for key splits of at least this many keys (a
+// request that splits, so that every unit streams that many), 32x32x16 for shorter ones and
+// for requests that do not split (see qk16_block).
+constexpr int64_t kQk16MinChunk = 1024;
+static bool use_qk16(const AttnArgs &a) { return a.S > 1 && a.chunk >= kQk16MinChunk; }
+
 hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype, int64_t units, hipStream_t st) {
     const dim3 grid((unsigned)units), block(256);
     const bool kimi_dims = dtype == KDT_BF16 && d_latent == 512 && d_rope == 64;
@@ -1956,7 +2060,10 @@ hipError_t launch_attend(const AttnArgs &a, int d_latent, int d_rope, int dtype,
     // GPU) a request has at most 64 rows, its one tile at rt = 0
     if (a.tile_rows == 2 * kRowsPerWave) {
         if (!kimi_dims) return hipErrorInvalidValue;
-        decode_attn_kernel<512, 64><<<grid, block, 0, st>>>(a);
+        if (use_qk16(a))
+            decode_attn_kernel<512, 64, false, true><<<grid, block, 0, st>>>(a);
+        else
+            decode_attn_kernel<512, 64><<<grid, block, 0, st>>>(a);
     } else if (kimi_dims && a.R <= 2 * kRowsPerWave)
         decode_attn_kernel<512, 64><<<grid, block, 0, st>>>(a);
     else if (kimi_dims)
@@ -2005,7 +2112,9 @@ hipError_t launch_attend_fused(AttnArgs a, const kdt_verify_desc &d, const Geome
     f.fd_per = make_fastdiv((uint32_t)f.per);
     f.fd_bs = make_fastdiv((uint32_t)f.bs);
     f.fd_gr = make_fastdiv((uint32_t)f.GR);
-    if (g.tile_rows == 2 * kRowsPerWave)
+    if (g.tile_rows == 2 * kRowsPerWave && use_qk16(a))
+        decode_attn_kernel<512, 64, true, true><<<dim3((unsigned)g.units), dim3(256), 0, st>>>(a);
+    else if (g.tile_rows == 2 * kRowsPerWave)
         decode_attn_kernel<512, 64, true><<<dim3((unsigned)g.units), dim3(256), 0, st>>>(a);
     else
         verify_attn_kernel<__bf16, 512, 64, true><<<dim3((unsigned)g.units), dim3(256), 0, st>>>(a);
