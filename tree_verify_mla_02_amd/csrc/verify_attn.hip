@@ -690,17 +690,18 @@ struct NoFill {
 // The S^T chain keeps its accumulator in VGPRs (the softmax reads it with VALU ops) while the
 // 256 AGPRs hold O^T.  Compiler-selected MFMAs in a kernel that uses AGPRs all write AGPRs,
 // which would push part of O^T out, so these MFMAs are written out with explicit register
-// classes.  The wait states the compiler would insert are spelled out: 2 between dependent
-// 32x32x16 MFMAs on the same accumulator (s_nop 1), 12 or more before a VALU instruction
-// reads the result (s_nop 7 + s_nop 4 after the last one).  The first MFMA takes srcC = 0.
+// classes.  The wait states the compiler would insert are spelled out: none between dependent
+// 32x32x16 MFMAs on the same accumulator (also with LDS reads between them; the compiler's own
+// chains of the builtin have none), 12 before a VALU instruction reads the result (s_nop 7 +
+// s_nop 4 after the last one: 13).  The first MFMA takes srcC = 0.
 template <int WAIT>
 __device__ __forceinline__ void mfma_s_first(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\ts_nop 1"
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
                  : "=&v"(acc) : "v"(a), "v"(b), "i"(WAIT));
 }
 template <int WAIT>
 __device__ __forceinline__ void mfma_s_next(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 1"
+    asm volatile("s_waitcnt lgkmcnt(%3)\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                  : "+v"(acc) : "v"(a), "v"(b), "i"(WAIT));
 }
 template <int WAIT>
