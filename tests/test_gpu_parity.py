@@ -104,6 +104,11 @@ SMALL = {
     # heads; over a long one a 128-row tile is one node
     "h128_t64": (workloads.Spec("h128a", 68, 1, 32, 128, 512, 64, "bf16", 3000, depth=6, topk=8), None),
     "h128_t128": (workloads.Spec("h128b", 69, 1, 32, 128, 512, 64, "bf16", 10000, depth=6, topk=8), None),
+    # the 64-row kernel's 16x16x32 S^T chain (key splits of at least 1024 keys): the Kimi shape
+    # with outliers, so that softmax references move; and 2048 rows over 8192 keys (8 splits)
+    "kimi_outliers": (workloads.Spec("kimi_o", 74, 1, 64, 64, 512, 64, "bf16", 4096, outlier_p=0.01), None),
+    "qk16_s8": (workloads.Spec("q16s8", 75, 1, 32, 64, 512, 64, "bf16", 8192, tree="random", outlier_p=0.005),
+                None),
 }
 
 
@@ -115,7 +120,7 @@ def test_small_all_rows(name):
 
 
 @pytest.mark.parametrize("name", ["split", "nodes256", "chain_short", "dec_tree60", "rows1000_long", "h128_t64",
-                                  "h128_t128"])
+                                  "h128_t128", "kimi_outliers"])
 def test_small_one_launch(name):
     """The one-request cases through kdt_tree_verify_prepare_attend (masks, plan and attention in
     one launch), every row against the oracle."""
