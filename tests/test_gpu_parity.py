@@ -109,6 +109,9 @@ SMALL = {
     "kimi_outliers": (workloads.Spec("kimi_o", 74, 1, 64, 64, 512, 64, "bf16", 4096, outlier_p=0.01), None),
     "qk16_s8": (workloads.Spec("q16s8", 75, 1, 32, 64, 512, 64, "bf16", 8192, tree="random", outlier_p=0.005),
                 None),
+    # the same chain with a partial last row tile (4000 rows) and a two-tile tree whose keys have
+    # places in the split range (125 nodes: 5 splits of 1216 keys)
+    "qk16_partial": (workloads.Spec("q16p", 76, 1, 125, 32, 512, 64, "bf16", 6000, tree="random"), None),
 }
 
 
@@ -120,7 +123,7 @@ def test_small_all_rows(name):
 
 
 @pytest.mark.parametrize("name", ["split", "nodes256", "chain_short", "dec_tree60", "rows1000_long", "h128_t64",
-                                  "h128_t128", "kimi_outliers"])
+                                  "h128_t128", "kimi_outliers", "qk16_partial"])
 def test_small_one_launch(name):
     """The one-request cases through kdt_tree_verify_prepare_attend (masks, plan and attention in
     one launch), every row against the oracle."""
