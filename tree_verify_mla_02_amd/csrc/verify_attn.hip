@@ -1439,11 +1439,12 @@ __device__ __forceinline__ void qk_block(const LDS_AS char *const (&pq)[Sh::CB /
 // registers (odd 16-lane rows of the first operand exchanged with even rows of the second)
 // leaves every lane its row l % 32 and keys 8*(i/4) + 4*(l/32) + i%4: the 32x32x16 chain's
 // layout, with the same scores bit for bit (checked on the GPU on the Kimi, decode, 7-node,
-// outlier and ragged shapes).  Used for long key splits, where it measured faster (a Kimi-shape launch, 16 tiles
-// per workgroup: 51.4 against 52.3 us); on 4-tile splits (a decode step, the 7-node block) the
-// 32x32x16 chain measured faster (21.7 against 22.2 us).  Running the next half's softmax
-// steps in this chain's shadow measured slower than both: a 16-cycle MFMA leaves too few issue
-// slots for them.
+// outlier, ragged and 128-node shapes).  Used for long key splits, where it measured faster (a
+// Kimi-shape launch, 16 tiles per workgroup: 51.4 against 52.3 us, 53.8 against 54.4 us on
+// another GPU); on 4-tile splits (a decode step, the 7-node block) the 32x32x16 chain measured
+// faster (21.7 against 22.2 us).  Running the first half's softmax steps in the shadow of the
+// second half's MFMAs measured slower than both, one step per MFMA or per two: a 16-cycle MFMA
+// leaves too few issue slots for them.
 
 // The VGPR-accumulator MFMA of this chain (see the S^T chain above for why asm).  A chain
 // alternating two accumulators needs no wait states between MFMAs; WAIT < 0: no LDS wait.
