@@ -53,7 +53,8 @@ extern "C" {
 typedef enum {
     KDT_OK = 0,
     KDT_ERR_INVALID_ARG = 1,   /* null pointer, negative or inconsistent size */
-    KDT_ERR_UNSUPPORTED = 2,   /* dims / dtype combination not built, N outside [1, 256] */
+    KDT_ERR_UNSUPPORTED = 2,   /* dims / dtype combination not built, N outside [1, 256],
+                                  max_cache_len above 2^30 keys */
     KDT_ERR_MISALIGNED = 3,    /* base pointer not 16-byte aligned or stride not a 16-byte multiple */
     KDT_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than kdt_tree_verify_workspace_size() */
     KDT_ERR_HIP = 5            /* a HIP runtime call or kernel launch failed */
@@ -79,7 +80,7 @@ typedef struct kdt_verify_desc {
     int32_t d_latent;           /* d_c: latent width (value width) */
     int32_t d_rope;             /* d_r: rotary key width */
     int32_t dtype;              /* kdt_dtype */
-    int64_t max_cache_len;      /* host bound: every cache_lens[b] <= max_cache_len */
+    int64_t max_cache_len;      /* host bound: every cache_lens[b] <= max_cache_len (at most 2^30) */
     int64_t total_cache_len;    /* rows present in ckv_cache / krope_cache (>= sum cache_lens) */
     int64_t q_lat_stride;       /* elements between consecutive (b,i,h) rows of q_lat  (>= d_c) */
     int64_t q_rope_stride;      /* elements between consecutive (b,i,h) rows of q_rope (>= d_r) */

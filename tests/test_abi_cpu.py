@@ -79,6 +79,8 @@ def test_prepare_rejects_bad_arguments_on_host():
     ("d_latent", 256, _lib.KDT_ERR_UNSUPPORTED), ("dtype", 7, _lib.KDT_ERR_UNSUPPORTED),
     ("ckv_stride", 500, _lib.KDT_ERR_INVALID_ARG), ("ckv_stride", 570, _lib.KDT_ERR_MISALIGNED), ("q_lat_stride", 516, _lib.KDT_ERR_MISALIGNED),
     ("max_cache_len", -1, _lib.KDT_ERR_INVALID_ARG),
+    # the plan's 32-bit split counts take lengths up to 2^30 keys; beyond int32 the length is invalid
+    ("max_cache_len", (1 << 30) + 1, _lib.KDT_ERR_UNSUPPORTED), ("max_cache_len", 1 << 31, _lib.KDT_ERR_INVALID_ARG),
 ])
 def test_desc_validation_on_host(field, value, code):
     d = _lib.VerifyDesc(batch=1, num_nodes=8, num_heads=4, d_latent=512, d_rope=64, dtype=_lib.KDT_BF16,
