@@ -1441,7 +1441,8 @@ __device__ __forceinline__ void qk_block(const LDS_AS char *const (&pq)[Sh::CB /
 // layout, with the same scores bit for bit (checked on the GPU on the Kimi, decode, 7-node,
 // outlier, ragged and 128-node shapes).  Used for long key splits, where it measured faster (a
 // Kimi-shape launch, 16 tiles per workgroup: 51.4 against 52.3 us, 53.8 against 54.4 us on
-// another GPU); on 4-tile splits (a decode step, the 7-node block) the 32x32x16 chain measured
+// another GPU, 54.2 against 54.9 us against the chain without wait states between its MFMAs);
+// on 4-tile splits (a decode step, the 7-node block) the 32x32x16 chain measured
 // faster (21.7 against 22.2 us).  Running the first half's softmax steps in the shadow of the
 // second half's MFMAs measured slower than both, one step per MFMA or per two: a 16-cycle MFMA
 // leaves too few issue slots for them.
