@@ -1904,7 +1904,7 @@ __global__ __launch_bounds__(64 * (WS > kWaves ? WS : kWaves)) void combine_kern
     constexpr int U = 8;                              // splits in flight per wave
     float2 ml[U];
     float4 x[U][GC];
-    // The first U splits' loads go out before the plan's verdict and the request's split count
+    // The first U splits' loads go out before the plan's validity flag and the request's split count
     // arrive (splits the request does not have are read from the workspace and ignored): the
     // merge waits for one memory round trip instead of two.
 #pragma unroll
